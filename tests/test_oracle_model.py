@@ -1,0 +1,262 @@
+"""Pins for the oracle's transformer math (CPU only).
+
+Each test checks the oracle against something other than itself: a library
+routine that computes the same definition (torch on the CPU, float64), a
+brute-force loop on a tiny case, a closed form, or an equality the method
+itself claims (selective batching == each request alone == padding+masking;
+garden.houmin.site/infra/orca section 3.1.2).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import model as om
+from orca_selective_iteration_amd import synth
+
+pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
+
+
+def rel_err(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+def f64_params(hin):
+    return [{k: v.astype(np.float64) for k, v in p.items()} for p in hin.params]
+
+
+def f64_caches(hin):
+    return [[(k.astype(np.float64), v.astype(np.float64)) for k, v in per] for per in hin.caches]
+
+
+def reqs_of(w):
+    return [om.Req(o, q, kv) for o, q, kv in zip(w.q_offset, w.q_len, w.kv_len)]
+
+
+# ------------------------------------------------------------ element-wise ops
+
+def test_layer_norm_matches_torch():
+    rng = np.random.default_rng(1)
+    z = rng.standard_normal((9, 48)) * 3 + 0.5
+    g = 1 + 0.1 * rng.standard_normal(48)
+    b = 0.1 * rng.standard_normal(48)
+    ref = F.layer_norm(torch.from_numpy(z), (48,), torch.from_numpy(g), torch.from_numpy(b),
+                       eps=1e-5).numpy()
+    assert rel_err(om.layer_norm(z, g, b, 1e-5), ref) < 1e-13
+
+
+def test_gelu_matches_torch_tanh_form():
+    z = np.linspace(-8, 8, 2001)
+    ref = F.gelu(torch.from_numpy(z), approximate="tanh").numpy()
+    assert np.max(np.abs(om.gelu_tanh(z) - ref)) < 1e-14
+    # the erf form differs by ~1e-3 somewhere: the oracle must not be it
+    erf_form = F.gelu(torch.from_numpy(z)).numpy()
+    assert np.max(np.abs(om.gelu_tanh(z) - erf_form)) > 1e-5
+    assert om.gelu_tanh(np.array([0.0]))[0] == 0.0
+
+
+def test_linear_matches_torch_and_is_not_transposed():
+    rng = np.random.default_rng(2)
+    a = rng.standard_normal((5, 7))
+    w = rng.standard_normal((11, 7))          # [out, in], not square
+    b = rng.standard_normal(11)
+    ref = F.linear(torch.from_numpy(a), torch.from_numpy(w), torch.from_numpy(b)).numpy()
+    assert om.linear(a, w, b).shape == (5, 11)
+    assert rel_err(om.linear(a, w, b), ref) < 1e-14
+
+
+# ---------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("q_len,heads,d", [(1, 1, 4), (5, 2, 8), (17, 4, 16)])
+def test_initiation_attention_is_causal_sdpa(q_len, heads, d):
+    rng = np.random.default_rng(3)
+    h = heads * d
+    q, k, v = (rng.standard_normal((q_len, h)) for _ in range(3))
+    out = om.request_attention(q, k, v, 0, heads)
+    t = lambda a: torch.from_numpy(a).view(q_len, heads, d).transpose(0, 1)
+    ref = F.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=True)
+    ref = ref.transpose(0, 1).reshape(q_len, h).numpy()
+    assert rel_err(out, ref) < 1e-13
+
+
+@pytest.mark.parametrize("kv_len,q_len", [(1, 1), (7, 1), (3, 4), (12, 5)])
+def test_attention_with_cache_matches_brute_force_loops(kv_len, q_len):
+    """Pure-Python loops over keys, query by query, head by head."""
+    rng = np.random.default_rng(4)
+    heads, d = 2, 4
+    h = heads * d
+    q = rng.standard_normal((q_len, h))
+    k = rng.standard_normal((kv_len + q_len, h))
+    v = rng.standard_normal((kv_len + q_len, h))
+    out = om.request_attention(q, k, v, kv_len, heads)
+    for j in range(q_len):
+        for hh in range(heads):
+            scores = []
+            for t in range(kv_len + j + 1):
+                s = sum(q[j, hh * d + e] * k[t, hh * d + e] for e in range(d))
+                scores.append(s / math.sqrt(d))
+            mx = max(scores)
+            ws = [math.exp(s - mx) for s in scores]
+            tot = sum(ws)
+            for e in range(d):
+                ref = sum(w * v[t, hh * d + e] for t, w in enumerate(ws)) / tot
+                assert abs(out[j, hh * d + e] - ref) < 1e-12
+
+
+def test_single_key_returns_value_row():
+    rng = np.random.default_rng(5)
+    q, k, v = (rng.standard_normal((1, 12)) for _ in range(3))
+    assert np.array_equal(om.request_attention(q, k, v, 0, 3), v)
+
+
+def test_identical_keys_average_values():
+    rng = np.random.default_rng(6)
+    kv_len, h = 6, 8
+    q = rng.standard_normal((1, h))
+    k = np.tile(rng.standard_normal((1, h)), (kv_len + 1, 1))
+    v = rng.standard_normal((kv_len + 1, h))
+    out = om.request_attention(q, k, v, kv_len, 2)
+    assert rel_err(out, v.mean(axis=0, keepdims=True)) < 1e-13
+
+
+# ------------------------------------------------------- whole layer vs torch
+
+def test_initiation_layer_matches_torch_pre_ln_decoder_block():
+    """A prompt-only request through one oracle layer equals torch's
+    pre-LayerNorm transformer layer with a causal mask, fed the same weights
+    (Q|K|V blocked in_proj, biases everywhere, tanh GeLU, eps 1e-5)."""
+    w = synth.custom_workload(1, 32, 4, 128, "f32", [9], [0])
+    hin = synth.host_inputs(w, seed=7)
+    p = f64_params(hin)[0]
+    x = hin.x.astype(np.float64)
+    y, app = om.selective_iteration([p], reqs_of(w), x, f64_caches(hin), w.heads, 1e-5)
+
+    layer = torch.nn.TransformerEncoderLayer(
+        d_model=32, nhead=4, dim_feedforward=128, dropout=0.0,
+        activation=lambda t: F.gelu(t, approximate="tanh"), layer_norm_eps=1e-5,
+        batch_first=True, norm_first=True, dtype=torch.float64)
+    sd = {
+        "self_attn.in_proj_weight": p["w_qkv"], "self_attn.in_proj_bias": p["b_qkv"],
+        "self_attn.out_proj.weight": p["w_o"], "self_attn.out_proj.bias": p["b_o"],
+        "linear1.weight": p["w_1"], "linear1.bias": p["b_1"],
+        "linear2.weight": p["w_2"], "linear2.bias": p["b_2"],
+        "norm1.weight": p["ln1_g"], "norm1.bias": p["ln1_b"],
+        "norm2.weight": p["ln2_g"], "norm2.bias": p["ln2_b"]}
+    layer.load_state_dict({k: torch.from_numpy(v) for k, v in sd.items()})
+    layer.train(False)
+    mask = torch.nn.Transformer.generate_square_subsequent_mask(9, dtype=torch.float64)
+    with torch.no_grad():
+        ref = layer(torch.from_numpy(x)[None], src_mask=mask, is_causal=True)[0].numpy()
+    assert rel_err(y, ref) < 1e-12
+    # the appended keys/values are the K and V blocks of the QKV projection
+    a = F.layer_norm(torch.from_numpy(x), (32,), torch.from_numpy(p["ln1_g"]),
+                     torch.from_numpy(p["ln1_b"]), eps=1e-5)
+    kv = F.linear(a, torch.from_numpy(p["w_qkv"]), torch.from_numpy(p["b_qkv"])).numpy()
+    assert rel_err(app[0][0][0], kv[:, 32:64]) < 1e-13
+    assert rel_err(app[0][0][1], kv[:, 64:96]) < 1e-13
+
+
+# ------------------------------------------- equalities the method claims (C2)
+
+def _mixed_workload(layers=2):
+    # increments with caches of 3 and 4, initiations of 2 and 3 (the figure),
+    # plus a 1-token initiation and a longer increment
+    return synth.custom_workload(layers, 32, 4, 64, "f32",
+                                 [1, 1, 1, 2, 3, 1], [3, 4, 9, 0, 0, 0])
+
+
+@pytest.mark.parametrize("layers", [1, 2])
+def test_selective_equals_alone_equals_padded(layers):
+    w = _mixed_workload(layers)
+    hin = synth.host_inputs(w, seed=8)
+    p, c, x = f64_params(hin), f64_caches(hin), hin.x.astype(np.float64)
+    reqs = reqs_of(w)
+    y, app = om.selective_iteration(p, reqs, x, c, w.heads, 1e-5)
+    y1, app1 = om.each_request_alone(p, reqs, x, c, w.heads, 1e-5)
+    y2, app2 = om.padded_masked(p, reqs, x, c, w.heads, 1e-5)
+    assert rel_err(y1, y) < 1e-12 and rel_err(y2, y) < 1e-12
+    for l in range(layers):
+        for i in range(len(reqs)):
+            for s in range(2):
+                assert rel_err(app1[l][i][s], app[l][i][s]) < 1e-12
+                assert rel_err(app2[l][i][s], app[l][i][s]) < 1e-12
+
+
+def test_tiny_figure_batch_equalities():
+    w = synth.workload("tiny-fp32")
+    assert w.rows == 7 and w.q_len == [1, 1, 2, 3] and w.kv_len == [3, 4, 0, 0]
+    hin = synth.host_inputs(w, seed=0)
+    p, c, x = f64_params(hin), f64_caches(hin), hin.x.astype(np.float64)
+    reqs = reqs_of(w)
+    y, _ = om.selective_iteration(p, reqs, x, c, w.heads, 1e-5)
+    y1, _ = om.each_request_alone(p, reqs, x, c, w.heads, 1e-5)
+    y2, _ = om.padded_masked(p, reqs, x, c, w.heads, 1e-5)
+    assert y.shape == (7, 64)
+    assert rel_err(y1, y) < 1e-12 and rel_err(y2, y) < 1e-12
+
+
+def test_permutation_invariance():
+    w = _mixed_workload(2)
+    hin = synth.host_inputs(w, seed=9)
+    p, c, x = f64_params(hin), f64_caches(hin), hin.x.astype(np.float64)
+    reqs = reqs_of(w)
+    y, _ = om.selective_iteration(p, reqs, x, c, w.heads, 1e-5)
+    order = [4, 0, 5, 2, 1, 3]
+    q2 = [w.q_len[i] for i in order]
+    kv2 = [w.kv_len[i] for i in order]
+    off, reqs2, xs = 0, [], []
+    for i, qq, kk in zip(order, q2, kv2):
+        reqs2.append(om.Req(off, qq, kk))
+        xs.append(x[reqs[i].q_offset:reqs[i].q_offset + qq])
+        off += qq
+    c2 = [[c[l][i] for i in order] for l in range(2)]
+    yp, _ = om.selective_iteration(p, reqs2, np.concatenate(xs), c2, w.heads, 1e-5)
+    for pos, i in enumerate(order):
+        a = yp[reqs2[pos].q_offset:reqs2[pos].q_offset + reqs2[pos].q_len]
+        b = y[reqs[i].q_offset:reqs[i].q_offset + reqs[i].q_len]
+        assert rel_err(a, b) < 1e-12
+
+
+@pytest.mark.parametrize("split", [0, 1, 4, 7])
+def test_prefix_invariance(split):
+    """Initiation of P tokens == initiation of k tokens then P-k increments
+    fed the same rows (the K/V manager appends; the position offset and the
+    mask of every increment must line up)."""
+    P, layers = 8, 2
+    w = synth.custom_workload(layers, 32, 4, 64, "f32", [P], [0])
+    hin = synth.host_inputs(w, seed=10)
+    p, x = f64_params(hin), hin.x.astype(np.float64)
+    empty = [[(np.zeros((0, 32)), np.zeros((0, 32)))] for _ in range(layers)]
+    y_full, app_full = om.selective_iteration(p, [om.Req(0, P, 0)], x, empty, 4, 1e-5)
+    k0 = max(split, 1)
+    ys = []
+    y, app = om.selective_iteration(p, [om.Req(0, k0, 0)], x[:k0], empty, 4, 1e-5)
+    ys.append(y)
+    cache = [[app[l][0]] for l in range(layers)]
+    for j in range(k0, P):
+        y, app = om.selective_iteration(p, [om.Req(0, 1, j)], x[j:j + 1], cache, 4, 1e-5)
+        ys.append(y)
+        cache = [[(np.concatenate([cache[l][0][0], app[l][0][0]]),
+                   np.concatenate([cache[l][0][1], app[l][0][1]]))] for l in range(layers)]
+    assert rel_err(np.concatenate(ys), y_full) < 1e-12
+    for l in range(layers):
+        assert rel_err(cache[l][0][0], app_full[l][0][0]) < 1e-12
+        assert rel_err(cache[l][0][1], app_full[l][0][1]) < 1e-12
+
+
+# ----------------------------------------------------------- shape pins
+
+def test_shape_pins_of_the_figure():
+    """[7,H] in, [7,3H] after the fused QKV Linear, [7,H] after the merge
+    (houmin 3.1.2); [5,H] for x3+x4 alone; 128+64+256 = 448 rows
+    (estelledc case 2)."""
+    w = synth.workload("tiny-fp32")
+    hin = synth.host_inputs(w)
+    p = hin.params[0]
+    a = om.layer_norm(hin.x, p["ln1_g"], p["ln1_b"], 1e-5)
+    assert om.linear(a, p["w_qkv"], p["b_qkv"]).shape == (7, 3 * 64)
+    assert sum(w.q_len[2:]) == 5
+    w448 = synth.custom_workload(1, 8, 2, 16, "f32", [128, 64, 256], [0, 0, 0])
+    assert w448.rows == 448 and w448.q_offset == [0, 128, 192]
