@@ -1,0 +1,303 @@
+/*
+ * orca.h - C ABI of liborca.so: one Orca iteration over an arbitrary mixed
+ * batch, computed by selective batching, on one MI355X (gfx950).
+ *
+ * Sources of the operations (page, section):
+ *   [houmin]      garden.houmin.site/infra/orca - 3.1.1 iteration-level
+ *                 scheduling; 3.1.2 selective batching.
+ *   [0h-n0]       0h-n0.github.io Orca digest - "Selective Batching",
+ *                 "Scheduler algorithm", "Implementation notes".
+ *   [arcsin2]     unpurerationalist.github.io ORCA notes - 3.2, 4.1, 4.2.
+ *   [ultralytics] ultralytics.com glossary "Continuous Batching" - limits
+ *                 (per-step token cap).
+ *
+ * Conventions for every entry point
+ *   - Sizes are element counts unless a name ends in _bytes.
+ *   - "device" pointers are HIP device memory owned by the caller; the
+ *     library only borrows them and never frees them.  "host" pointers are
+ *     read during the call only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     GPU entry points only enqueue work on it and never synchronise it;
+ *     their results are valid once the stream has reached that point.
+ *   - Every argument is validated on the host before anything is enqueued;
+ *     a failed check returns ORCA_ERR_INVALID (or ORCA_ERR_UNSUPPORTED for a
+ *     shape the kernels do not implement) and has no side effect.
+ *     orca_last_error() then describes the failure.
+ *   - A HIP runtime failure while enqueuing returns ORCA_ERR_HIP.
+ *   - Handles are not thread-safe: one context per stream / thread.
+ *
+ * Data types.  ORCA_F32: fp32 everywhere.  ORCA_BF16: bf16 storage for
+ * weights, activations and the K/V pools; fp32 accumulation in every
+ * contraction, fp32 LayerNorm statistics, fp32 softmax, an fp32 residual
+ * stream inside the iteration; values are rounded to nearest-even at each
+ * bf16 store.
+ */
+#ifndef ORCA_H
+#define ORCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ORCA_OK = 0,
+  ORCA_ERR_INVALID = 1,     /* bad argument / descriptor; nothing enqueued */
+  ORCA_ERR_NOSPACE = 2,     /* K/V allocator: no contiguous range large enough */
+  ORCA_ERR_HIP = 3,         /* the HIP runtime reported an error */
+  ORCA_ERR_UNSUPPORTED = 4  /* valid, but a shape the kernels do not cover */
+} orca_status;
+
+typedef enum { ORCA_F32 = 0, ORCA_BF16 = 1 } orca_dtype;
+
+/* [houmin] 3.1.2: a request is in the initiation phase while the K/V manager
+ * holds no cache for it (all prompt tokens are processed at once), and in
+ * the increment phase afterwards (one token per iteration). */
+typedef enum { ORCA_INITIATION = 0, ORCA_INCREMENT = 1 } orca_phase;
+
+/* Human-readable name of a status code (static storage). */
+const char* orca_status_str(orca_status s);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* orca_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Attention K/V manager: token-granular allocator over one K/V pool
+ * ([0h-n0] implementation notes: the pool is allocated once at start-up
+ * because dynamic device malloc/free is too slow; an index table records
+ * where each request's entries live; [houmin] 3.1.1: entries are released
+ * as soon as a request finishes).  Host memory only; no GPU call.
+ * ---------------------------------------------------------------------- */
+typedef struct orca_kv orca_kv;
+
+/* New allocator over token slots [0, capacity).  capacity >= 0. */
+orca_status orca_kv_create(int64_t capacity, orca_kv** out);
+void        orca_kv_destroy(orca_kv* kv);
+
+/* Reserve n_tokens >= 1 contiguous slots at the lowest base that fits
+ * (first fit).  *out_base receives the base.  ORCA_ERR_NOSPACE if no free
+ * range is large enough (the state is unchanged). */
+orca_status orca_kv_alloc(orca_kv* kv, int64_t n_tokens, int64_t* out_base);
+
+/* Release the reservation that starts at `base`; the freed range coalesces
+ * with free neighbours.  ORCA_ERR_INVALID if `base` starts no reservation. */
+orca_status orca_kv_free(orca_kv* kv, int64_t base);
+
+/* Slots currently reserved, and the capacity. */
+int64_t orca_kv_used(const orca_kv* kv);
+int64_t orca_kv_capacity(const orca_kv* kv);
+
+/* Length of the reservation starting at `base`, or -1 if there is none. */
+int64_t orca_kv_reservation(const orca_kv* kv, int64_t base);
+
+/* ------------------------------------------------------------------------
+ * Engine: the model, its K/V pools and one iteration.
+ * ---------------------------------------------------------------------- */
+
+/* Decoder shape.  head dim d = hidden / heads.  Supported: hidden % 64 == 0,
+ * ffn % 64 == 0; bf16 needs d in {64, 128}; fp32 needs d in {16, 32, 64, 128}. */
+typedef struct {
+  int32_t layers;
+  int32_t hidden;       /* H */
+  int32_t heads;
+  int32_t ffn;          /* F */
+  int32_t dtype;        /* orca_dtype */
+  float   ln_eps;       /* LayerNorm epsilon (inside the square root) */
+  int64_t kv_capacity;  /* token slots per layer and head in each pool */
+} orca_model_desc;
+
+/* One layer's parameters, device pointers of the model dtype.  The block is
+ * a pre-LayerNorm decoder layer ([houmin] 3.1.2 lists LayerNorm, the QKV
+ * projection, attention, the output projection, GeLU and residual adds):
+ *   a  = LN(x; ln1_g, ln1_b)
+ *   [q|k|v] = a W_qkv^T + b_qkv      W_qkv [3H][H]: rows 0..H-1 produce Q,
+ *                                    H..2H-1 K, 2H..3H-1 V; head h owns
+ *                                    columns h*d .. h*d+d-1 of each block
+ *   o  = per-request attention of q over the request's own K/V
+ *   h1 = x + o W_o^T + b_o           W_o [H][H]
+ *   c  = LN(h1; ln2_g, ln2_b)
+ *   f  = GeLU_tanh(c W_1^T + b_1)    W_1 [F][H]
+ *   y  = h1 + f W_2^T + b_2          W_2 [H][F]
+ * Every W is stored row-major [out][in]; vectors are [out]. */
+typedef struct {
+  const void *ln1_g, *ln1_b, *w_qkv, *b_qkv, *w_o, *b_o;
+  const void *ln2_g, *ln2_b, *w_1, *b_1, *w_2, *b_2;
+} orca_layer_weights;
+
+/* One request of the batch ([arcsin2] 4.1: the engine receives per request
+ * its id, token index and phase).  Host memory.
+ *   q_offset, q_len  rows [q_offset, q_offset+q_len) of the flattened
+ *                    [sum L, H] input; offsets must be contiguous from 0
+ *   kv_len           K/V entries cached before this iteration
+ *   phase            ORCA_INITIATION (kv_len == 0) or ORCA_INCREMENT
+ *                    (kv_len >= 1, q_len == 1)
+ *   kv_base          first pool slot of the request's reservation; its
+ *                    entry t lives in slot kv_base + t; this iteration
+ *                    appends slots kv_base+kv_len .. kv_base+kv_len+q_len-1 */
+typedef struct {
+  int32_t q_offset;
+  int32_t q_len;
+  int32_t kv_len;
+  int32_t phase;
+  int64_t kv_base;
+} orca_req_desc;
+
+typedef struct orca_ctx orca_ctx;
+
+/* Create an engine.
+ *   desc        model shape (copied)
+ *   layers      host array [desc->layers] of device weight pointers (copied;
+ *               the weights themselves are borrowed)
+ *   k_pool,
+ *   v_pool      device [layers][heads][kv_capacity][d] of the model dtype
+ *               (borrowed); entry t of head h of a request at layer l is
+ *               pool[l][h][kv_base + t][0..d-1]
+ *   kv          optional (may be NULL) allocator whose capacity equals
+ *               desc->kv_capacity; when given, every request's range
+ *               kv_base .. kv_base+kv_len+q_len-1 must lie inside one of its
+ *               reservations (borrowed; must outlive the context)
+ *   max_rows,
+ *   max_reqs    largest sum L and request count any iteration will use;
+ *               they size the workspace and the pinned metadata buffers
+ * Allocates pinned host staging memory (hipHostMalloc); no device memory. */
+orca_status orca_create(const orca_model_desc* desc, const orca_layer_weights* layers,
+                        void* k_pool, void* v_pool, const orca_kv* kv,
+                        int32_t max_rows, int32_t max_reqs, orca_ctx** out);
+orca_status orca_destroy(orca_ctx* ctx);
+
+/* Bytes of device workspace an iteration needs (activations, the fp32
+ * residual stream, split-attention partials, metadata).  The caller
+ * allocates it once; 256-byte alignment is required. */
+size_t orca_workspace_bytes(const orca_ctx* ctx);
+
+/* Run one iteration of every layer over the batch ([houmin] 3.1.1: the
+ * scheduler invokes the engine for exactly one iteration; 3.1.2: LayerNorm,
+ * the four Linear layers, GeLU and residual adds run on the flattened
+ * [sum L, H] matrix; attention is split per request and merged back).
+ *   reqs, n_reqs  host array of request descriptors (validated, see above)
+ *   x             device [sum L][H] model dtype: input rows
+ *   y             device [sum L][H] model dtype: output rows of the last
+ *                 layer (may not alias x or the workspace)
+ *   workspace     device, >= orca_workspace_bytes(ctx) bytes
+ * Appends the K/V rows of every request to the pools, at every layer.
+ * Metadata goes to the device with one asynchronous copy from a pinned
+ * ring of staging buffers; the call does not wait for the GPU except when
+ * the ring slot it needs is still being copied from. */
+orca_status orca_iteration(orca_ctx* ctx, const orca_req_desc* reqs, int32_t n_reqs,
+                           const void* x, void* y, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
+ * Single-step entry points: the kernels orca_iteration launches, one step
+ * of the layer at a time, with the same launch configuration.  For tests
+ * and kernel timing.
+ * ---------------------------------------------------------------------- */
+
+/* out[r] = LN(x[r]; gamma, beta) for rows 0..rows-1.  x device fp32
+ * [rows][hidden] (the residual stream); gamma, beta device [hidden] and out
+ * device [rows][hidden] of `dtype`.  Statistics in fp32, population
+ * variance.  ([0h-n0] implementation notes: fused LayerNorm.) */
+orca_status orca_op_layernorm(int32_t dtype, const float* x, const void* gamma,
+                              const void* beta, void* out, int32_t rows, int32_t hidden,
+                              float eps, void* stream);
+
+/* Epilogues of the flattened Linear layers ([houmin] 3.1.2). */
+typedef enum {
+  ORCA_EPI_BIAS = 0,       /* out[m][n] = acc + bias[n]            (dtype) */
+  ORCA_EPI_BIAS_GELU = 1,  /* out[m][n] = GeLU_tanh(acc + bias[n]) (dtype) */
+  ORCA_EPI_BIAS_RESID = 2  /* out[m][n] += acc + bias[n]  (out is fp32)    */
+} orca_epilogue;
+
+/* acc[m][n] = sum_k a[m][k] * w[n][k] on a device [m][k], w device [n][k],
+ * bias device [n] (all `dtype`), then the epilogue.  m >= 0; n % 64 == 0 and
+ * k % 64 == 0.  bf16 runs on the MFMA units. */
+orca_status orca_op_linear(int32_t dtype, int32_t epilogue, const void* a, const void* w,
+                           const void* bias, void* out, int32_t m, int32_t n, int32_t k,
+                           void* stream);
+
+/* The fused QKV projection with the K/V manager's append: for every row m,
+ * [q|k|v] = a[m] W_qkv^T + b_qkv; q goes to q_out[m][0..H-1]; k and v of
+ * head h go to k_pool_l[h][row_dst[m]][..] and v_pool_l[h][row_dst[m]][..].
+ * row_dst: device int32 [m], each in [0, kv_capacity).  k_pool_l/v_pool_l
+ * point at one layer's pool [heads][kv_capacity][d].  ([houmin] 3.1.2: the
+ * QKV Linear yields 3H columns; the split before attention is index
+ * arithmetic; the new K/V of every token is appended to its request.) */
+orca_status orca_op_qkv(int32_t dtype, const void* a, const void* w_qkv, const void* b_qkv,
+                        void* q_out, void* k_pool_l, void* v_pool_l, const int32_t* row_dst,
+                        int32_t m, int32_t hidden, int32_t heads, int64_t kv_capacity,
+                        void* stream);
+
+/* Split attention of one layer ([houmin] 3.1.2): every request attends
+ * separately over its own K/V (initiation: causal over its prompt;
+ * increment: one query over kv_len cached entries plus its own new one);
+ * outputs land at the request's own rows of o (the merge is index
+ * arithmetic).  q, o device [sum L][H] of the context's dtype; the new K/V
+ * rows must already be in the pools (orca_op_qkv).  Uses the context's
+ * pools at `layer` and its metadata path; workspace as for orca_iteration. */
+orca_status orca_op_attention(orca_ctx* ctx, int32_t layer, const orca_req_desc* reqs,
+                              int32_t n_reqs, const void* q, void* o, void* workspace,
+                              size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Iteration-level scheduler ([houmin] 3.1.1; [0h-n0] scheduler algorithm;
+ * [arcsin2] 4.2).  Host only.  Each step:
+ *   1. the batch returned by the previous step counts as executed: each
+ *      member produced one token, its kv_len grew by its q_len;
+ *   2. finished requests (generated == out_len) leave and their K/V
+ *      reservation is released at once (policy 1: only when every member
+ *      of the running batch has finished);
+ *   3. requests with arrival <= now join the FCFS queue;
+ *   4. FCFS admission while the batch has fewer than max_batch requests:
+ *      the head is admitted if the batch's rows (1 per continuing request +
+ *      the prompts admitted so far + its prompt) stay <= token_budget, its
+ *      reservation prompt_len + max_tokens fits the free slot count, and a
+ *      contiguous range exists; the first miss ends admission (no skipping);
+ *      policy 1 admits only when no batch is running;
+ *   5. the batch is emitted: continuing requests (increment, admission
+ *      order), then this step's admissions (initiation).
+ * ---------------------------------------------------------------------- */
+typedef struct orca_sched orca_sched;
+
+enum { ORCA_POLICY_ITERATION = 0, ORCA_POLICY_STATIC = 1 };
+
+/* kv: the allocator reservations come from (borrowed); its capacity is the
+ * scheduler's K/V slot budget. */
+orca_status orca_sched_create(orca_kv* kv, int32_t max_batch, int32_t token_budget,
+                              int32_t policy, orca_sched** out);
+void        orca_sched_destroy(orca_sched* s);
+
+/* Queue a request.  out_len is the output length (the request finishes
+ * after producing out_len tokens; the policy never reads it ahead of time).
+ * ORCA_ERR_INVALID if the id is taken, a length is < 1, out_len > max_tokens,
+ * prompt_len > token_budget or prompt_len + max_tokens > the K/V capacity. */
+orca_status orca_sched_submit(orca_sched* s, int64_t id, double arrival, int32_t prompt_len,
+                              int32_t max_tokens, int32_t out_len);
+
+/* One scheduling step at time `now`.  Writes up to `cap` descriptors (host)
+ * and their request ids; *n_out = batch size (0: nothing to run now).
+ * ORCA_ERR_INVALID if cap < max_batch. */
+orca_status orca_sched_step(orca_sched* s, double now, orca_req_desc* out, int64_t* out_ids,
+                            int32_t cap, int32_t* n_out);
+
+/* 1 when nothing is queued, waiting or running. */
+int32_t orca_sched_idle(const orca_sched* s);
+
+/* Earliest arrival not yet queued; ORCA_ERR_INVALID if there is none. */
+orca_status orca_sched_next_arrival(const orca_sched* s, double* t);
+
+/* Per-request record: iteration index (0-based, counting non-empty steps)
+ * of its initiation, of its last token, and of the step that released it;
+ * -1 where not reached.  ORCA_ERR_INVALID for an unknown id. */
+orca_status orca_sched_request_info(const orca_sched* s, int64_t id, int64_t* admitted_at,
+                                    int64_t* finished_at, int64_t* released_at);
+
+/* Slots reserved by running requests. */
+int64_t orca_sched_used(const orca_sched* s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ORCA_H */

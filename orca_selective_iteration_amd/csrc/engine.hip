@@ -1,0 +1,448 @@
+// The engine behind orca_iteration: descriptor validation, the per-iteration
+// metadata (one asynchronous copy from a pinned ring), and the layer loop
+// that launches the gfx950 kernels on the caller's stream.
+//
+// garden.houmin.site/infra/orca 3.1.1: the scheduler hands the engine one
+// iteration of a selected batch; 3.1.2: non-attention operations run on the
+// flattened [sum L, H] matrix, attention per request (split / merge are
+// index arithmetic here).  unpurerationalist.github.io ORCA notes 4.1: the
+// engine receives per request its token index and phase, and the host never
+// waits for the GPU to hand over this metadata.  0h-n0.github.io digest,
+// implementation notes: the K/V pool is allocated once, an index table
+// records each request's slots (here: kv_base + position).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "kernels.h"
+#include "kv.h"
+#include "orca.h"
+#include "status.h"
+
+using namespace orca;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int NSLOT = 4;
+
+size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+size_t dsize(int dtype) { return dtype == ORCA_BF16 ? 2 : 4; }
+
+bool head_dim_ok(int dtype, int d) {
+  if (dtype == ORCA_BF16) return d == 64 || d == 128;
+  return d == 16 || d == 32 || d == 64 || d == 128;
+}
+
+}  // namespace
+
+struct orca_ctx {
+  orca_model_desc desc{};
+  std::vector<orca_layer_weights> layers;
+  void* k_pool = nullptr;
+  void* v_pool = nullptr;
+  const orca_kv* kv = nullptr;
+  int32_t max_rows = 0, max_reqs = 0;
+  int64_t max_items = 0;
+  int device = 0;
+  // workspace layout
+  size_t off_resid = 0, off_a = 0, off_q = 0, off_o = 0, off_f = 0;
+  size_t off_part_o = 0, off_part_ml = 0, off_meta = 0, ws_bytes = 0, meta_bytes = 0;
+  // pinned staging ring for the metadata
+  void* staging[NSLOT] = {};
+  hipEvent_t ev[NSLOT] = {};
+  bool ev_live[NSLOT] = {};
+  int slot = 0;
+  std::vector<std::pair<int64_t, int64_t>> ranges;   // scratch for validation
+
+  size_t layer_pool_elems() const {
+    return (size_t)desc.heads * (size_t)desc.kv_capacity * (size_t)(desc.hidden / desc.heads);
+  }
+};
+
+namespace {
+
+// Host-side plan of one iteration, written straight into a pinned slot.
+struct Plan {
+  DevReq* reqs;
+  int32_t* row_dst;
+  SplitItem* items;
+  SplitRow* srows;
+  PrefillItem* pf;
+  int n_reqs = 0, rows = 0, n_items = 0, n_srows = 0, n_pf = 0;
+  size_t off_reqs = 0, off_row_dst = 0, off_items = 0, off_srows = 0, off_pf = 0, bytes = 0;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Validates the descriptors; on success returns ORCA_OK and the row count.
+orca_status validate(orca_ctx* c, const orca_req_desc* reqs, int32_t n, int32_t* rows_out,
+                     int64_t* items_out) {
+  ORCA_CHECK_ARG(n >= 0 && n <= c->max_reqs, "batch of %d requests (max_reqs %d)", n,
+                 c->max_reqs);
+  ORCA_CHECK_ARG(n == 0 || reqs != nullptr, "reqs is NULL");
+  int64_t off = 0, items = 0;
+  c->ranges.clear();
+  for (int i = 0; i < n; ++i) {
+    const orca_req_desc& r = reqs[i];
+    ORCA_CHECK_ARG(r.q_offset == off, "request %d: q_offset %d, expected %lld (contiguous)", i,
+                   r.q_offset, (long long)off);
+    ORCA_CHECK_ARG(r.q_len >= 1, "request %d: q_len %d < 1", i, r.q_len);
+    ORCA_CHECK_ARG(r.kv_len >= 0, "request %d: kv_len %d < 0", i, r.kv_len);
+    if (r.phase == ORCA_INITIATION) {
+      ORCA_CHECK_ARG(r.kv_len == 0, "request %d: initiation with kv_len %d (a request with a "
+                     "cache is in the increment phase)", i, r.kv_len);
+    } else {
+      ORCA_CHECK_ARG(r.phase == ORCA_INCREMENT, "request %d: unknown phase %d", i, r.phase);
+      ORCA_CHECK_ARG(r.kv_len >= 1, "request %d: increment without a cache", i);
+      ORCA_CHECK_ARG(r.q_len == 1, "request %d: increment with q_len %d", i, r.q_len);
+    }
+    const int64_t lo = r.kv_base, hi = r.kv_base + int64_t(r.kv_len) + r.q_len;
+    ORCA_CHECK_ARG(lo >= 0 && hi <= c->desc.kv_capacity,
+                   "request %d: slots [%lld, %lld) outside the pool of %lld", i, (long long)lo,
+                   (long long)hi, (long long)c->desc.kv_capacity);
+    if (c->kv)
+      ORCA_CHECK_ARG(c->kv->covers(lo, hi), "request %d: slots [%lld, %lld) are not inside one "
+                     "K/V reservation", i, (long long)lo, (long long)hi);
+    c->ranges.emplace_back(lo, hi);
+    off += r.q_len;
+    if (r.phase == ORCA_INCREMENT || c->desc.dtype == ORCA_F32) {
+      for (int j = 0; j < r.q_len; ++j) items += ceil_div(int64_t(r.kv_len) + j + 1, SPLIT_CHUNK);
+    } else {
+      for (int j = 0; j < r.q_len; ++j) items += ceil_div(int64_t(j) + 1, SPLIT_CHUNK);
+    }
+  }
+  ORCA_CHECK_ARG(off <= c->max_rows, "batch of %lld rows (max_rows %d)", (long long)off,
+                 c->max_rows);
+  std::sort(c->ranges.begin(), c->ranges.end());
+  for (size_t i = 1; i < c->ranges.size(); ++i)
+    ORCA_CHECK_ARG(c->ranges[i - 1].second <= c->ranges[i].first,
+                   "two requests use overlapping K/V slots near %lld",
+                   (long long)c->ranges[i].first);
+  ORCA_CHECK_ARG(items <= c->max_items, "batch needs %lld attention work items, the workspace "
+                 "holds %lld", (long long)items, (long long)c->max_items);
+  *rows_out = int32_t(off);
+  *items_out = items;
+  return ORCA_OK;
+}
+
+// Lays the plan out in `buf` (packed, 16-byte aligned sections).
+void build_plan(const orca_ctx* c, const orca_req_desc* reqs, int32_t n, int32_t rows,
+                int64_t n_items, char* buf, Plan& p) {
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = (o + bytes + 15) / 16 * 16;
+    return at;
+  };
+  p.off_reqs = take(sizeof(DevReq) * n);
+  p.off_row_dst = take(sizeof(int32_t) * rows);
+  p.off_items = take(sizeof(SplitItem) * n_items);
+  p.off_srows = take(sizeof(SplitRow) * rows);
+  p.off_pf = 0;
+  p.bytes = o;
+  p.reqs = reinterpret_cast<DevReq*>(buf + p.off_reqs);
+  p.row_dst = reinterpret_cast<int32_t*>(buf + p.off_row_dst);
+  p.items = reinterpret_cast<SplitItem*>(buf + p.off_items);
+  p.srows = reinterpret_cast<SplitRow*>(buf + p.off_srows);
+  p.pf = nullptr;
+  p.n_reqs = n;
+  p.rows = rows;
+  int ni = 0, ns = 0;
+  for (int i = 0; i < n; ++i) {
+    const orca_req_desc& r = reqs[i];
+    p.reqs[i] = DevReq{r.q_offset, r.q_len, r.kv_len, r.phase, r.kv_base};
+    for (int j = 0; j < r.q_len; ++j) {
+      const int row = r.q_offset + j;
+      const int64_t pos = int64_t(r.kv_len) + j;
+      p.row_dst[row] = int32_t(r.kv_base + pos);
+      const int keys = int(pos + 1);
+      const int chunks = int(ceil_div(keys, SPLIT_CHUNK));
+      p.srows[ns++] = SplitRow{row, ni, chunks, i};
+      for (int ch = 0; ch < chunks; ++ch)
+        p.items[ni++] = SplitItem{row, i, ch * SPLIT_CHUNK, std::min(keys, (ch + 1) * SPLIT_CHUNK)};
+    }
+  }
+  p.n_items = ni;
+  p.n_srows = ns;
+  (void)c;
+}
+
+orca_status hip_fail(hipError_t e, const char* what) {
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return ORCA_ERR_HIP;
+}
+
+#define HIP_TRY(expr, what)                        \
+  do {                                             \
+    hipError_t _e = (expr);                        \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+// Validates, stages and uploads the metadata; fills device-side pointers.
+orca_status stage(orca_ctx* c, const orca_req_desc* reqs, int32_t n, char* ws, hipStream_t s,
+                  Plan& p, AttnArgs& aa) {
+  int32_t rows = 0;
+  int64_t n_items = 0;
+  orca_status st = validate(c, reqs, n, &rows, &n_items);
+  if (st != ORCA_OK) return st;
+  const int slot = c->slot;
+  c->slot = (c->slot + 1) % NSLOT;
+  if (c->ev_live[slot]) HIP_TRY(hipEventSynchronize(c->ev[slot]), "metadata ring wait");
+  char* host = static_cast<char*>(c->staging[slot]);
+  build_plan(c, reqs, n, rows, n_items, host, p);
+  char* dev = ws + c->off_meta;
+  if (p.bytes > 0) {
+    HIP_TRY(hipMemcpyAsync(dev, host, p.bytes, hipMemcpyHostToDevice, s), "metadata upload");
+    HIP_TRY(hipEventRecord(c->ev[slot], s), "metadata event");
+    c->ev_live[slot] = true;
+  }
+  const orca_model_desc& d = c->desc;
+  aa = AttnArgs{};
+  aa.dtype = d.dtype;
+  aa.hidden = d.hidden;
+  aa.heads = d.heads;
+  aa.head_dim = d.hidden / d.heads;
+  aa.cap = d.kv_capacity;
+  aa.reqs = reinterpret_cast<const DevReq*>(dev + p.off_reqs);
+  aa.items = reinterpret_cast<const SplitItem*>(dev + p.off_items);
+  aa.n_items = p.n_items;
+  aa.srows = reinterpret_cast<const SplitRow*>(dev + p.off_srows);
+  aa.n_srows = p.n_srows;
+  aa.pf = nullptr;
+  aa.n_pf = 0;
+  aa.part_o = reinterpret_cast<float*>(ws + c->off_part_o);
+  aa.part_ml = reinterpret_cast<float*>(ws + c->off_part_ml);
+  return ORCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+orca_status orca_create(const orca_model_desc* desc, const orca_layer_weights* layers,
+                        void* k_pool, void* v_pool, const orca_kv* kv, int32_t max_rows,
+                        int32_t max_reqs, orca_ctx** out) {
+  ORCA_CHECK_ARG(desc && layers && k_pool && v_pool && out, "orca_create: NULL argument");
+  const orca_model_desc& d = *desc;
+  ORCA_CHECK_ARG(d.dtype == ORCA_F32 || d.dtype == ORCA_BF16, "unknown dtype %d", d.dtype);
+  ORCA_CHECK_ARG(d.layers >= 1 && d.hidden >= 64 && d.heads >= 1 && d.ffn >= 64,
+                 "bad shape layers %d hidden %d heads %d ffn %d", d.layers, d.hidden, d.heads,
+                 d.ffn);
+  ORCA_CHECK_ARG(d.hidden % d.heads == 0, "hidden %d not divisible by heads %d", d.hidden,
+                 d.heads);
+  ORCA_CHECK_ARG(d.ln_eps > 0.f, "ln_eps must be > 0");
+  ORCA_CHECK_ARG(d.kv_capacity >= 1 && d.kv_capacity < (int64_t(1) << 31),
+                 "kv_capacity %lld out of range", (long long)d.kv_capacity);
+  ORCA_CHECK_ARG(max_rows >= 1 && max_reqs >= 1, "max_rows / max_reqs must be >= 1");
+  ORCA_CHECK_ARG(!kv || kv->capacity == d.kv_capacity, "allocator capacity %lld != pool %lld",
+                 (long long)(kv ? kv->capacity : 0), (long long)d.kv_capacity);
+  if (d.hidden % 64 || d.ffn % 64 || d.hidden > 12288 || !head_dim_ok(d.dtype, d.hidden / d.heads)) {
+    set_error("unsupported shape: hidden %d ffn %d head_dim %d", d.hidden, d.ffn,
+              d.hidden / d.heads);
+    return ORCA_ERR_UNSUPPORTED;
+  }
+  for (int l = 0; l < d.layers; ++l) {
+    const orca_layer_weights& w = layers[l];
+    ORCA_CHECK_ARG(w.ln1_g && w.ln1_b && w.w_qkv && w.b_qkv && w.w_o && w.b_o && w.ln2_g &&
+                   w.ln2_b && w.w_1 && w.b_1 && w.w_2 && w.b_2, "layer %d: NULL weight", l);
+  }
+  auto* c = new (std::nothrow) orca_ctx;
+  ORCA_CHECK_ARG(c != nullptr, "out of host memory");
+  c->desc = d;
+  c->layers.assign(layers, layers + d.layers);
+  c->k_pool = k_pool;
+  c->v_pool = v_pool;
+  c->kv = kv;
+  c->max_rows = max_rows;
+  c->max_reqs = max_reqs;
+  // every row yields at most 1 + keys / SPLIT_CHUNK items; increment keys
+  // lie in disjoint pool ranges; initiation rows of one prompt add a
+  // triangle (bounded by max_rows^2 / 2)
+  c->max_items = int64_t(max_rows) + d.kv_capacity / SPLIT_CHUNK + 1 +
+                 (int64_t(max_rows) * max_rows / 2) / SPLIT_CHUNK + max_rows;
+  const size_t R = max_rows, H = d.hidden, F = d.ffn, s = dsize(d.dtype);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  c->off_resid = take(R * H * 4);
+  c->off_a = take(R * H * s);
+  c->off_q = take(R * H * s);
+  c->off_o = take(R * H * s);
+  c->off_f = take(R * F * s);
+  c->off_part_o = take(size_t(c->max_items) * H * 4);
+  c->off_part_ml = take(size_t(c->max_items) * d.heads * 2 * 4);
+  c->meta_bytes = sizeof(DevReq) * max_reqs + sizeof(int32_t) * R +
+                  sizeof(SplitItem) * c->max_items + sizeof(SplitRow) * R + 16 * 8;
+  c->off_meta = take(c->meta_bytes);
+  c->ws_bytes = o;
+  hipError_t e = hipGetDevice(&c->device);
+  for (int i = 0; i < NSLOT && e == hipSuccess; ++i) {
+    e = hipHostMalloc(&c->staging[i], c->meta_bytes, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming);
+  }
+  if (e != hipSuccess) {
+    orca_destroy(c);
+    return hip_fail(e, "orca_create");
+  }
+  *out = c;
+  return ORCA_OK;
+}
+
+orca_status orca_destroy(orca_ctx* c) {
+  if (!c) return ORCA_OK;
+  for (int i = 0; i < NSLOT; ++i) {
+    if (c->ev[i]) {
+      (void)hipEventSynchronize(c->ev[i]);
+      (void)hipEventDestroy(c->ev[i]);
+    }
+    if (c->staging[i]) (void)hipHostFree(c->staging[i]);
+  }
+  delete c;
+  return ORCA_OK;
+}
+
+size_t orca_workspace_bytes(const orca_ctx* c) { return c ? c->ws_bytes : 0; }
+
+static orca_status check_ws(const orca_ctx* c, const void* ws, size_t ws_bytes) {
+  ORCA_CHECK_ARG(ws != nullptr, "workspace is NULL");
+  ORCA_CHECK_ARG(reinterpret_cast<uintptr_t>(ws) % ALIGN == 0, "workspace not 256-byte aligned");
+  ORCA_CHECK_ARG(ws_bytes >= c->ws_bytes, "workspace of %zu bytes, need %zu", ws_bytes,
+                 c->ws_bytes);
+  return ORCA_OK;
+}
+
+static orca_status run_attention(orca_ctx* c, int layer, AttnArgs aa, const void* q, void* o,
+                                 hipStream_t s) {
+  const size_t pool = c->layer_pool_elems() * dsize(c->desc.dtype);
+  aa.q = q;
+  aa.o = o;
+  aa.k_pool = static_cast<char*>(c->k_pool) + pool * layer;
+  aa.v_pool = static_cast<char*>(c->v_pool) + pool * layer;
+  HIP_TRY(launch_attention(aa, s), "attention launch");
+  return ORCA_OK;
+}
+
+orca_status orca_iteration(orca_ctx* c, const orca_req_desc* reqs, int32_t n_reqs, const void* x,
+                           void* y, void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  ORCA_CHECK_ARG(c != nullptr, "NULL context");
+  orca_status st = check_ws(c, workspace, ws_bytes);
+  if (st != ORCA_OK) return st;
+  ORCA_CHECK_ARG(n_reqs == 0 || (x && y), "x / y is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  Plan p;
+  AttnArgs aa;
+  st = stage(c, reqs, n_reqs, ws, s, p, aa);
+  if (st != ORCA_OK || p.rows == 0) return st;
+
+  const orca_model_desc& d = c->desc;
+  const int R = p.rows, H = d.hidden, F = d.ffn, dt = d.dtype;
+  float* resid = reinterpret_cast<float*>(ws + c->off_resid);
+  void* a = ws + c->off_a;
+  void* q = ws + c->off_q;
+  void* o = ws + c->off_o;
+  void* f = ws + c->off_f;
+  const int32_t* row_dst = reinterpret_cast<const int32_t*>(ws + c->off_meta + p.off_row_dst);
+  const size_t pool = c->layer_pool_elems() * dsize(dt);
+
+  HIP_TRY(launch_to_f32(dt, x, resid, int64_t(R) * H, s), "input conversion");
+  for (int l = 0; l < d.layers; ++l) {
+    const orca_layer_weights& w = c->layers[l];
+    QkvDest qd{q, static_cast<char*>(c->k_pool) + pool * l, static_cast<char*>(c->v_pool) + pool * l,
+               row_dst, H, H / d.heads, d.kv_capacity};
+    HIP_TRY(launch_layernorm(dt, resid, w.ln1_g, w.ln1_b, a, R, H, d.ln_eps, s), "LN1");
+    HIP_TRY(launch_linear(dt, EPI_QKV, a, w.w_qkv, w.b_qkv, nullptr, &qd, R, 3 * H, H, s), "QKV");
+    st = run_attention(c, l, aa, q, o, s);
+    if (st != ORCA_OK) return st;
+    HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_RESID, o, w.w_o, w.b_o, resid, nullptr, R, H, H, s),
+            "output projection");
+    HIP_TRY(launch_layernorm(dt, resid, w.ln2_g, w.ln2_b, a, R, H, d.ln_eps, s), "LN2");
+    HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_GELU, a, w.w_1, w.b_1, f, nullptr, R, F, H, s), "FFN1");
+    HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_RESID, f, w.w_2, w.b_2, resid, nullptr, R, H, F, s),
+            "FFN2");
+  }
+  HIP_TRY(launch_from_f32(dt, resid, y, int64_t(R) * H, s), "output conversion");
+  return ORCA_OK;
+}
+
+// ------------------------------------------------------------ single steps
+
+orca_status orca_op_layernorm(int32_t dtype, const float* x, const void* gamma, const void* beta,
+                              void* out, int32_t rows, int32_t hidden, float eps, void* stream) {
+  clear_error();
+  ORCA_CHECK_ARG(dtype == ORCA_F32 || dtype == ORCA_BF16, "unknown dtype %d", dtype);
+  ORCA_CHECK_ARG(rows >= 0 && hidden >= 4 && hidden % 4 == 0 && hidden <= 12288,
+                 "rows %d hidden %d (hidden must be a multiple of 4, at most 12288)", rows, hidden);
+  ORCA_CHECK_ARG(eps > 0.f, "eps must be > 0");
+  ORCA_CHECK_ARG(rows == 0 || (x && gamma && beta && out), "NULL argument");
+  HIP_TRY(launch_layernorm(dtype, x, gamma, beta, out, rows, hidden, eps,
+                           static_cast<hipStream_t>(stream)), "layernorm launch");
+  return ORCA_OK;
+}
+
+orca_status orca_op_linear(int32_t dtype, int32_t epilogue, const void* a, const void* w,
+                           const void* bias, void* out, int32_t m, int32_t n, int32_t k,
+                           void* stream) {
+  clear_error();
+  ORCA_CHECK_ARG(dtype == ORCA_F32 || dtype == ORCA_BF16, "unknown dtype %d", dtype);
+  ORCA_CHECK_ARG(epilogue >= ORCA_EPI_BIAS && epilogue <= ORCA_EPI_BIAS_RESID,
+                 "unknown epilogue %d", epilogue);
+  ORCA_CHECK_ARG(m >= 0 && n >= 64 && k >= 64, "shape m %d n %d k %d", m, n, k);
+  if (n % 64 || k % 64) {
+    set_error("unsupported shape: n %d and k %d must be multiples of 64", n, k);
+    return ORCA_ERR_UNSUPPORTED;
+  }
+  ORCA_CHECK_ARG(m == 0 || (a && w && bias && out), "NULL argument");
+  HIP_TRY(launch_linear(dtype, epilogue, a, w, bias, out, nullptr, m, n, k,
+                        static_cast<hipStream_t>(stream)), "linear launch");
+  return ORCA_OK;
+}
+
+orca_status orca_op_qkv(int32_t dtype, const void* a, const void* w_qkv, const void* b_qkv,
+                        void* q_out, void* k_pool_l, void* v_pool_l, const int32_t* row_dst,
+                        int32_t m, int32_t hidden, int32_t heads, int64_t kv_capacity,
+                        void* stream) {
+  clear_error();
+  ORCA_CHECK_ARG(dtype == ORCA_F32 || dtype == ORCA_BF16, "unknown dtype %d", dtype);
+  ORCA_CHECK_ARG(m >= 0 && hidden >= 64 && heads >= 1 && hidden % heads == 0 && kv_capacity >= 1,
+                 "shape m %d hidden %d heads %d capacity %lld", m, hidden, heads,
+                 (long long)kv_capacity);
+  if (hidden % 64 || !head_dim_ok(dtype, hidden / heads)) {
+    set_error("unsupported shape: hidden %d head_dim %d", hidden, hidden / heads);
+    return ORCA_ERR_UNSUPPORTED;
+  }
+  ORCA_CHECK_ARG(m == 0 || (a && w_qkv && b_qkv && q_out && k_pool_l && v_pool_l && row_dst),
+                 "NULL argument");
+  QkvDest qd{q_out, k_pool_l, v_pool_l, row_dst, hidden, hidden / heads, kv_capacity};
+  HIP_TRY(launch_linear(dtype, EPI_QKV, a, w_qkv, b_qkv, nullptr, &qd, m, 3 * hidden, hidden,
+                        static_cast<hipStream_t>(stream)), "qkv launch");
+  return ORCA_OK;
+}
+
+orca_status orca_op_attention(orca_ctx* c, int32_t layer, const orca_req_desc* reqs,
+                              int32_t n_reqs, const void* q, void* o, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  clear_error();
+  ORCA_CHECK_ARG(c != nullptr, "NULL context");
+  ORCA_CHECK_ARG(layer >= 0 && layer < c->desc.layers, "layer %d out of range", layer);
+  orca_status st = check_ws(c, workspace, ws_bytes);
+  if (st != ORCA_OK) return st;
+  ORCA_CHECK_ARG(n_reqs == 0 || (q && o), "q / o is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Plan p;
+  AttnArgs aa;
+  st = stage(c, reqs, n_reqs, static_cast<char*>(workspace), s, p, aa);
+  if (st != ORCA_OK || p.rows == 0) return st;
+  return run_attention(c, layer, aa, q, o, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Host-side launchers of the gfx950 kernels (defined next to each kernel).
+// Every launcher enqueues on `stream`, assumes its arguments were validated
+// by the caller, and returns the hipError_t of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace orca {
+
+// ---- LayerNorm and conversions (ln.hip) ----------------------------------
+hipError_t launch_layernorm(int dtype, const float* x, const void* g, const void* b, void* out,
+                            int rows, int hidden, float eps, hipStream_t s);
+hipError_t launch_to_f32(int dtype, const void* in, float* out, int64_t n, hipStream_t s);
+hipError_t launch_from_f32(int dtype, const float* in, void* out, int64_t n, hipStream_t s);
+
+// ---- Linear layers (gemm.hip) ---------------------------------------------
+struct QkvDest {
+  void* q_out;          // [m][H]
+  void* k_pool;         // one layer: [heads][cap][d]
+  void* v_pool;
+  const int32_t* row_dst;
+  int hidden, head_dim;
+  int64_t cap;
+};
+// epilogue: ORCA_EPI_* or EPI_QKV (3).  For EPI_QKV, `out` is ignored and
+// `qkv` describes the destinations.
+constexpr int EPI_QKV = 3;
+hipError_t launch_linear(int dtype, int epilogue, const void* a, const void* w, const void* bias,
+                         void* out, const QkvDest* qkv, int m, int n, int k, hipStream_t s);
+
+// ---- Attention (attn.hip) --------------------------------------------------
+// Device request record: same layout as orca_req_desc.
+struct DevReq {
+  int32_t q_offset, q_len, kv_len, phase;
+  int64_t kv_base;
+};
+// Split-KV work item: query row `row` of request `req`, keys [c0, c1).
+struct SplitItem {
+  int32_t row, req, c0, c1;
+};
+// Query rows served by the split-KV path, with their item range.
+struct SplitRow {
+  int32_t row, item_begin, item_count, req;
+};
+// Prefill (initiation) tile: request `req`, query rows [q0, q1) of its prompt.
+struct PrefillItem {
+  int32_t req, q0, q1, pad;
+};
+
+struct AttnArgs {
+  int dtype, hidden, heads, head_dim;
+  int64_t cap;
+  const void* q;          // [rows][H]
+  void* o;                // [rows][H]
+  const void* k_pool;     // one layer: [heads][cap][d]
+  const void* v_pool;
+  const DevReq* reqs;
+  const SplitItem* items;  int n_items;
+  const SplitRow* srows;   int n_srows;
+  const PrefillItem* pf;   int n_pf;
+  float* part_o;          // [n_items][heads][d]
+  float* part_ml;         // [n_items][heads][2]
+};
+
+// Keys per split-KV work item for increment rows.
+constexpr int SPLIT_CHUNK = 512;
+// Query rows per prefill tile.
+constexpr int PREFILL_ROWS = 64;
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace orca

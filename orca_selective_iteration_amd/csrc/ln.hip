@@ -1,0 +1,139 @@
+// Fused LayerNorm over the flattened [sum L, H] rows, and dtype conversions
+// of the fp32 residual stream.
+//
+// 0h-n0.github.io Orca digest, implementation notes: LayerNorm statistics and
+// scaling run as one fused kernel.  garden.houmin.site/infra/orca 3.1.2:
+// LayerNorm mixes no tokens, so it runs on all rows of the batch at once.
+//
+// One 256-thread workgroup per row; the row stays in registers (16-byte
+// loads, fully coalesced) between the mean pass, the centred variance pass
+// and the normalise pass, so HBM sees one read of the fp32 row and one write
+// of the output row: (4 + sizeof(T)) * H bytes per row.
+#include "device.h"
+#include "kernels.h"
+#include "orca.h"
+
+namespace orca {
+
+constexpr int LN_THREADS = 256;
+constexpr int LN_MAX_VEC = 12;   // float4 per thread: H <= 12288
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < LN_THREADS / 64; ++i) t += red[i];
+  return t;
+}
+
+// 4 consecutive elements of T as a float4 (8- or 16-byte access).
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+}
+__device__ __forceinline__ void store4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ void store4(bf16* p, float4 v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+}
+
+template <typename T>
+__global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const float* __restrict__ x,
+                                                               const T* __restrict__ g,
+                                                               const T* __restrict__ b,
+                                                               T* __restrict__ out, int hidden,
+                                                               float eps) {
+  __shared__ float red[LN_THREADS / 64];
+  const int row = blockIdx.x;
+  const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * hidden);
+  const int nv = hidden / 4;
+  float4 v[LN_MAX_VEC];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < LN_MAX_VEC; ++i) {
+    const int c = threadIdx.x + i * LN_THREADS;
+    if (c < nv) {
+      v[i] = xr[c];
+      s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+  }
+  const float mean = block_sum(s, red) / hidden;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < LN_MAX_VEC; ++i) {
+    const int c = threadIdx.x + i * LN_THREADS;
+    if (c < nv) {
+      const float a = v[i].x - mean, bb = v[i].y - mean, cc = v[i].z - mean, d = v[i].w - mean;
+      q += (a * a + bb * bb) + (cc * cc + d * d);
+    }
+  }
+  const float rstd = rsqrtf(block_sum(q, red) / hidden + eps);
+#pragma unroll
+  for (int i = 0; i < LN_MAX_VEC; ++i) {
+    const int c = threadIdx.x + i * LN_THREADS;
+    if (c < nv) {
+      const float4 gg = load4(g + c * 4), bb = load4(b + c * 4);
+      float4 y;
+      y.x = (v[i].x - mean) * rstd * gg.x + bb.x;
+      y.y = (v[i].y - mean) * rstd * gg.y + bb.y;
+      y.z = (v[i].z - mean) * rstd * gg.z + bb.z;
+      y.w = (v[i].w - mean) * rstd * gg.w + bb.w;
+      store4(out + (size_t)row * hidden + c * 4, y);
+    }
+  }
+}
+
+template <typename T>
+__global__ void to_f32_kernel(const T* __restrict__ in, float* __restrict__ out, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = load_f32(in + i);
+}
+
+template <typename T>
+__global__ void from_f32_kernel(const float* __restrict__ in, T* __restrict__ out, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    store_f32(out + i, in[i]);
+}
+
+hipError_t launch_layernorm(int dtype, const float* x, const void* g, const void* b, void* out,
+                            int rows, int hidden, float eps, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (dtype == ORCA_BF16)
+    hipLaunchKernelGGL(layernorm_kernel<bf16>, dim3(rows), dim3(LN_THREADS), 0, s, x,
+                       (const bf16*)g, (const bf16*)b, (bf16*)out, hidden, eps);
+  else
+    hipLaunchKernelGGL(layernorm_kernel<float>, dim3(rows), dim3(LN_THREADS), 0, s, x,
+                       (const float*)g, (const float*)b, (float*)out, hidden, eps);
+  return hipGetLastError();
+}
+
+static dim3 grid_for(int64_t n) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  return dim3((unsigned)(blocks > 0 ? blocks : 1));
+}
+
+hipError_t launch_to_f32(int dtype, const void* in, float* out, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (dtype == ORCA_BF16)
+    hipLaunchKernelGGL(to_f32_kernel<bf16>, grid_for(n), dim3(256), 0, s, (const bf16*)in, out, n);
+  else
+    hipLaunchKernelGGL(to_f32_kernel<float>, grid_for(n), dim3(256), 0, s, (const float*)in, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_from_f32(int dtype, const float* in, void* out, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (dtype == ORCA_BF16)
+    hipLaunchKernelGGL(from_f32_kernel<bf16>, grid_for(n), dim3(256), 0, s, in, (bf16*)out, n);
+  else
+    hipLaunchKernelGGL(from_f32_kernel<float>, grid_for(n), dim3(256), 0, s, in, (float*)out, n);
+  return hipGetLastError();
+}
+
+}  // namespace orca
