@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Throughput of one selective-batched Orca iteration on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one orca_iteration over the whole mixed batch: every layer's
+LayerNorms, the four flattened Linear layers with their fused epilogues,
+the K/V append, and split attention (initiation prompts and increment
+tokens).  Inputs (weights, K/V caches, hidden rows) are seeded synthetic
+draws already resident in HBM when the timed region starts.
+
+Prints ONE JSON line: tokens processed per second (sum L per iteration over
+the timed iterations), the roofline of the dominant kernel (the FFN1 GEMM:
+MFMA-bound) and of decode attention (HBM-bound), both timed live with HIP
+events on the stream they run on, and the CPU oracle timed on one layer of
+the same batch on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+
+DEFAULT_WORKLOAD = "gpt13b-40l"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                   choices=["tiny-fp32", "h1024-2l", "gpt13b-40l", "gpt175b-8l"])
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--kernel-reps", type=int, default=20)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", choices=["iteration", "gemm", "decode"], default=None,
+                   help="run one timed region only (for profiling)")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_events(fn, reps, stream):
+    """Average milliseconds of fn() over `reps` back-to-back calls, bracketed
+    by HIP events recorded on `stream`."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def cpu_baseline(model, work, x_dev, layers_total):
+    """The CPU oracle on layer 0 of the same batch (all rows, all requests),
+    fp32 numpy on the host; tokens/s extrapolated to the model's depth."""
+    import numpy as np
+    from oracle import model as om
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    p = {k: v.float().cpu().numpy() for k, v in model.weights[0].items()}
+    x = x_dev.float().cpu().numpy()
+    caches = [[model.cache_rows(0, i, 0, work.kv_len[i]) for i in range(work.n_reqs)]]
+    reqs, off = [], 0
+    for q, kv in zip(work.q_len, work.kv_len):
+        reqs.append(om.Req(off, q, kv))
+        off += q
+    t0 = time.perf_counter()
+    om.selective_layer(p, reqs, x, caches[0], work.heads, work.eps)
+    dt = time.perf_counter() - t0
+    return {"value": work.rows / (dt * layers_total), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"layer 0 of {layers_total} ({work.rows} rows, {work.n_reqs} requests), "
+                      f"numpy fp32, {dt:.1f} s; extrapolated x{layers_total} layers"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the iteration has no multi-GPU path in this build)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from orca_selective_iteration_amd import lib as L
+    from orca_selective_iteration_amd import synth
+    from orca_selective_iteration_amd.runner import DeviceModel
+
+    torch.cuda.set_device(0)
+    work = synth.workload(args.workload, args.seed)
+    t0 = time.time()
+    host = synth.host_inputs(work, args.seed) if work.layers * work.hidden <= 4096 else None
+    model = DeviceModel(work, host=host, device="cuda", seed=args.seed, log=log)
+    if host is not None:
+        x = torch.from_numpy(host.x).to("cuda", model.tdt)
+    else:
+        x = synth.device_normal_(torch.empty((work.rows, work.hidden), dtype=model.tdt,
+                                             device="cuda"), args.seed * 31 + 5)
+    y = torch.empty_like(x)
+    reqs = model.descriptors()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f}s: {work.name} rows={work.rows} reqs={work.n_reqs} "
+        f"kv_tokens={sum(work.kv_len)} pool_slots={model.cap}")
+
+    def step():
+        model.iteration(reqs, x, y, stream)
+
+    res = {}
+    ms = None
+    if args.only in (None, "iteration"):
+        for _ in range(args.warmup):
+            step()
+        ms = time_events(step, args.steps, stream)
+        log(f"iteration: {ms:.3f} ms, {work.rows / ms * 1e3:.0f} tokens/s")
+
+    H, F, M = work.hidden, work.ffn, work.rows
+    bf16 = work.dtype == "bf16"
+    # dominant kernel: the FFN1 GEMM (M = sum L, N = F, K = H) with GeLU epilogue
+    gemm = None
+    if args.only in (None, "gemm"):
+        a = synth.device_normal_(torch.empty((M, H), dtype=model.tdt, device="cuda"), 11)
+        f = torch.empty((M, F), dtype=model.tdt, device="cuda")
+        w = model.weights[0]
+
+        def ffn1():
+            L.orca_op_linear(model.odt, L.ORCA_EPI_BIAS_GELU, a, w["w_1"], w["b_1"], f, M, F, H,
+                             stream)
+        for _ in range(3):
+            ffn1()
+        gms = time_events(ffn1, args.kernel_reps, stream)
+        tflops = 2.0 * M * F * H / (gms * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+        gemm = {"bound": "mfma", "kernel": "gemm_bf16_kernel<gelu> (FFN1)" if bf16 else
+                "gemm_f32_kernel<gelu> (FFN1)", "shape": [M, F, H],
+                "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tflops / peak, 4), "traffic": None, "ms_per_launch": round(gms, 4)}
+        log(f"FFN1 GEMM {M}x{F}x{H}: {gms:.3f} ms, {tflops:.1f} TFLOP/s")
+        del a, f
+
+    decode = None
+    incr = [i for i in range(work.n_reqs) if work.kv_len[i] > 0]
+    if args.only in (None, "decode") and incr:
+        d_reqs = model.descriptors(reqs=incr)
+        n = len(incr)
+        q = synth.device_normal_(torch.empty((n, H), dtype=model.tdt, device="cuda"), 13)
+        o = torch.empty_like(q)
+
+        def dec():
+            L.orca_op_attention(model.ctx, 0, d_reqs, q, o, model.ws, model.ws_bytes, stream)
+        for _ in range(3):
+            dec()
+        dms = time_events(dec, args.kernel_reps, stream)
+        esz = 2 if bf16 else 4
+        nbytes = sum(2 * (work.kv_len[i] + 1) * H * esz for i in incr)
+        gbs = nbytes / (dms * 1e-3) / 1e9
+        decode = {"bound": "hbm", "kernel": "attn_split_kernel + attn_combine_kernel "
+                  "(increment rows, one layer)", "achieved": round(gbs, 1),
+                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                  "traffic": None, "ms_per_launch": round(dms, 4),
+                  "algorithmic_bytes": nbytes}
+        log(f"decode attention ({n} requests, one layer): {dms:.3f} ms, {gbs:.0f} GB/s")
+
+    cpu = None
+    if args.only is None and not args.no_cpu_baseline:
+        t1 = time.time()
+        cpu = cpu_baseline(model, work, x, work.layers)
+        log(f"cpu baseline: {cpu['value']:.1f} tokens/s ({time.time() - t1:.1f}s)")
+
+    model.close()
+    if ms is None:
+        return
+    value = work.rows / (ms * 1e-3)
+    line = {
+        "metric": "processed tokens/s per mixed iteration (1 GPU)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded random-init weights, K/V caches and hidden rows)",
+        "config": {"workload": work.name, "layers": work.layers, "hidden": H,
+                   "heads": work.heads, "ffn": F, "sum_L": M, "requests": work.n_reqs,
+                   "initiation_requests": sum(1 for v in work.kv_len if v == 0),
+                   "increment_requests": len(incr), "cached_kv_tokens": sum(work.kv_len),
+                   "parallelism": "single GPU"},
+        "roofline": gemm,
+        "decode_attention": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,8 +33,9 @@ class DeviceModel:
     def __init__(self, work: Workload, host: Optional[HostInputs] = None, device: str = "cuda",
                  seed: int = 0, kv_capacity: Optional[int] = None, slack: int = 0,
                  max_rows: Optional[int] = None, max_reqs: Optional[int] = None,
-                 use_kv_manager: bool = True, fill_caches: bool = True):
+                 use_kv_manager: bool = True, fill_caches: bool = True, log=None):
         import torch
+        log = log or (lambda *a: None)
         self.work = work
         self.device = device
         self.tdt = torch_dtype(work.dtype)
@@ -47,8 +48,12 @@ class DeviceModel:
             self.weights = [{k: torch.from_numpy(np.ascontiguousarray(v)).to(device=device, dtype=self.tdt)
                              for k, v in p.items()} for p in host.params]
         else:
-            self.weights = [device_param_tensors(work, seed * 1000003 + l, device, self.tdt)
-                            for l in range(work.layers)]
+            self.weights = []
+            for l in range(work.layers):
+                self.weights.append(device_param_tensors(work, seed * 1000003 + l, device,
+                                                         self.tdt))
+                if l % 10 == 9:
+                    log(f"weights: {l + 1}/{work.layers} layers drawn")
         # pools [layers][heads][cap][d]
         shape = (work.layers, work.heads, self.cap, d)
         self.k_pool = torch.empty(shape, dtype=self.tdt, device=device)
@@ -67,7 +72,9 @@ class DeviceModel:
             if host is not None:
                 self.load_host_caches(host.caches)
             else:
+                log(f"filling K/V pools: 2 x {self.k_pool.numel() * self.k_pool.element_size() / 1e9:.1f} GB")
                 self.fill_device_caches(seed)
+                log("K/V pools filled")
         self.max_rows = int(max_rows or max(work.rows, 1))
         self.max_reqs = int(max_reqs or max(work.n_reqs, 1))
         self.ctx = L.orca_create(work.layers, work.hidden, work.heads, work.ffn, self.odt,
