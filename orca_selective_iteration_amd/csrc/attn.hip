@@ -172,8 +172,182 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------ prefill (MFMA)
+//
+// Initiation rows of a bf16 model: causal attention of a prompt over itself.
+// A 256-thread workgroup takes one head and PREFILL_ROWS = 128 consecutive
+// query positions of one request (32 per wave) and walks the request's keys
+// 0 .. last query position in steps of 64, staging each K step (row-major)
+// and V step (transposed to [d][key]) in LDS.  Scores are computed
+// transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: a lane then owns
+// one query (its column) and 16 of the 32 keys of each MFMA tile, so the
+// softmax max / sum need one cross-lane step (lane ^ 32).  The probabilities
+// feed O^T = V^T P^T straight from the score registers: the keys of the
+// PV MFMA's k-dimension are taken in the order in which the score tile
+// left them in the lanes (an order the V^T fragment reads follow), so P
+// never moves between lanes.  Online softmax in base 2 with a running max
+// and sum per query; the output tile is transposed through LDS so the
+// [sum L, H] rows are written with 16-byte stores.
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
+  constexpr int BQ = PREFILL_ROWS;       // 128 queries: 32 per wave
+  constexpr int BKV = 64;                // keys per step
+  constexpr int KLD = D + 8;             // K row stride (elements)
+  constexpr int VLD = BKV + 8;           // V^T row stride
+  constexpr int OLD = D + 8;             // output staging row stride
+  constexpr int KV_ELEMS = BKV * KLD + D * VLD;
+  constexpr int O_ELEMS = BQ * OLD;
+  constexpr int SMEM = KV_ELEMS > O_ELEMS ? KV_ELEMS : O_ELEMS;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
+  uint16_t* sK = smem;
+  uint16_t* sV = smem + BKV * KLD;
+
+  const PrefillItem it = a.pf[blockIdx.x];
+  const int h = blockIdx.y;
+  const DevReq rq = a.reqs[it.req];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const size_t H = (size_t)a.hidden;
+
+  // this lane's query: position qpos of the prompt (kv_len is 0)
+  const int qpos = it.q0 + w * 32 + col;
+  const int qrow = rq.q_offset + min(qpos, it.q1 - 1);
+  bf16x8_t qf[D / 16];
+  {
+    const bf16* qp = (const bf16*)a.q + (size_t)qrow * H + h * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
+  }
+  f32x16_t o[D / 32];
+#pragma unroll
+  for (int dm = 0; dm < D / 32; ++dm)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dm][r] = 0.f;
+  float m_run = NEG_BIG, l_run = 0.f;
+  const float sc = LOG2E / sqrtf((float)D);
+
+  const int kend = min(it.q1, it.q0 + BQ);              // keys the block needs
+  const int kend_wave = min(it.q1, it.q0 + w * 32 + 32);  // keys this wave needs
+  const size_t head_base = ((size_t)h * a.cap + (size_t)rq.kv_base) * D;
+  const bf16* kb = (const bf16*)a.k_pool + head_base;
+  const bf16* vb = (const bf16*)a.v_pool + head_base;
+
+  for (int k0 = 0; k0 < kend; k0 += BKV) {
+    __syncthreads();
+    for (int c = tid; c < BKV * (D / 8); c += 256) {
+      const int key = c / (D / 8), ch = c % (D / 8);
+      const int kk = min(k0 + key, kend - 1);
+      *reinterpret_cast<uint4*>(&sK[key * KLD + ch * 8]) =
+          *reinterpret_cast<const uint4*>(kb + (size_t)kk * D + ch * 8);
+    }
+    {
+      const int key = tid & 63;
+      const int kk = min(k0 + key, kend - 1);
+      for (int ch = tid >> 6; ch < D / 8; ch += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(vb + (size_t)kk * D + ch * 8);
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sV[(ch * 8 + 2 * j) * VLD + key] = uint16_t(wv[j] & 0xffffu);
+          sV[(ch * 8 + 2 * j + 1) * VLD + key] = uint16_t(wv[j] >> 16);
+        }
+      }
+    }
+    __syncthreads();
+    if (k0 >= kend_wave) continue;
+
+    // S^T = K Q^T for keys k0 .. k0+63 (two 32-key tiles)
+    f32x16_t s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8_t kf =
+            *reinterpret_cast<const bf16x8_t*>(&sK[(32 * t + col) * KLD + ks * 16 + half * 8]);
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
+      }
+    }
+    // causal mask, scale, running max
+    float mx = NEG_BIG;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
+        const bool vis = key <= qpos && key < kend;
+        s[t][r] = vis ? s[t][r] * sc : NEG_BIG;
+        mx = fmaxf(mx, s[t][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= corr;
+#pragma unroll
+    for (int dm = 0; dm < D / 32; ++dm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dm][r] *= corr;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = s[t][r] > 0.5f * NEG_BIG ? exp2f(s[t][r] - m_new) : 0.f;
+        s[t][r] = p;
+        l_run += p;
+      }
+    // O^T += V^T P^T, 16 keys per MFMA step
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int t = st >> 1, rb = (st & 1) * 8;
+      bf16x8_t pb;
+      {
+        uint32_t pk[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(s[t][rb + 2 * j], s[t][rb + 2 * j + 1]);
+        pb = *reinterpret_cast<const bf16x8_t*>(pk);
+      }
+#pragma unroll
+      for (int dm = 0; dm < D / 32; ++dm) {
+        const uint16_t* vr = &sV[(dm * 32 + col) * VLD + 16 * st + 4 * half];
+        uint32_t vk[4];
+        *reinterpret_cast<uint2*>(&vk[0]) = *reinterpret_cast<const uint2*>(vr);
+        *reinterpret_cast<uint2*>(&vk[2]) = *reinterpret_cast<const uint2*>(vr + 8);
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vk);
+        o[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[dm], 0, 0, 0);
+      }
+    }
+  }
+
+  // normalise, transpose through LDS, write the rows
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.f / l_tot;
+  __syncthreads();
+  uint16_t* sO = smem;
+#pragma unroll
+  for (int dm = 0; dm < D / 32; ++dm)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d = dm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      sO[(w * 32 + col) * OLD + d] = f32_to_bf16_bits(o[dm][r] * inv);
+    }
+  __syncthreads();
+  for (int c = tid; c < BQ * (D / 8); c += 256) {
+    const int ql = c / (D / 8), ch = c % (D / 8);
+    const int qp = it.q0 + ql;
+    if (qp < it.q1)
+      *reinterpret_cast<uint4*>((bf16*)a.o + (size_t)(rq.q_offset + qp) * H + h * D + ch * 8) =
+          *reinterpret_cast<const uint4*>(&sO[ql * OLD + ch * 8]);
+  }
+}
+
 template <typename T, int D>
 static void launch_split(const AttnArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (a.n_pf > 0)
+      hipLaunchKernelGGL((attn_prefill_kernel<D>), dim3(a.n_pf, a.heads), dim3(256), 0, s, a);
+  }
   if (a.n_items == 0) return;
   hipLaunchKernelGGL((attn_split_kernel<T, D>), dim3(a.n_items, a.heads), dim3(256), 0, s, a);
   hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3(a.n_srows, a.heads), dim3(D < 128 ? D : 128),

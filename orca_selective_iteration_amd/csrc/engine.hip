@@ -47,7 +47,7 @@ struct orca_ctx {
   void* v_pool = nullptr;
   const orca_kv* kv = nullptr;
   int32_t max_rows = 0, max_reqs = 0;
-  int64_t max_items = 0;
+  int64_t max_items = 0, max_pf = 0;
   int device = 0;
   // workspace layout
   size_t off_resid = 0, off_a = 0, off_q = 0, off_o = 0, off_f = 0;
@@ -79,13 +79,19 @@ struct Plan {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// bf16 initiation rows take the MFMA prefill kernel; every other row the
+// split-KV kernel.
+bool uses_prefill(const orca_ctx* c, const orca_req_desc& r) {
+  return c->desc.dtype == ORCA_BF16 && r.phase == ORCA_INITIATION;
+}
+
 // Validates the descriptors; on success returns ORCA_OK and the row count.
 orca_status validate(orca_ctx* c, const orca_req_desc* reqs, int32_t n, int32_t* rows_out,
-                     int64_t* items_out) {
+                     int64_t* items_out, int64_t* pf_out) {
   ORCA_CHECK_ARG(n >= 0 && n <= c->max_reqs, "batch of %d requests (max_reqs %d)", n,
                  c->max_reqs);
   ORCA_CHECK_ARG(n == 0 || reqs != nullptr, "reqs is NULL");
-  int64_t off = 0, items = 0;
+  int64_t off = 0, items = 0, pf = 0;
   c->ranges.clear();
   for (int i = 0; i < n; ++i) {
     const orca_req_desc& r = reqs[i];
@@ -110,10 +116,10 @@ orca_status validate(orca_ctx* c, const orca_req_desc* reqs, int32_t n, int32_t*
                      "K/V reservation", i, (long long)lo, (long long)hi);
     c->ranges.emplace_back(lo, hi);
     off += r.q_len;
-    if (r.phase == ORCA_INCREMENT || c->desc.dtype == ORCA_F32) {
-      for (int j = 0; j < r.q_len; ++j) items += ceil_div(int64_t(r.kv_len) + j + 1, SPLIT_CHUNK);
+    if (uses_prefill(c, r)) {
+      pf += ceil_div(r.q_len, PREFILL_ROWS);
     } else {
-      for (int j = 0; j < r.q_len; ++j) items += ceil_div(int64_t(j) + 1, SPLIT_CHUNK);
+      for (int j = 0; j < r.q_len; ++j) items += ceil_div(int64_t(r.kv_len) + j + 1, SPLIT_CHUNK);
     }
   }
   ORCA_CHECK_ARG(off <= c->max_rows, "batch of %lld rows (max_rows %d)", (long long)off,
@@ -123,16 +129,18 @@ orca_status validate(orca_ctx* c, const orca_req_desc* reqs, int32_t n, int32_t*
     ORCA_CHECK_ARG(c->ranges[i - 1].second <= c->ranges[i].first,
                    "two requests use overlapping K/V slots near %lld",
                    (long long)c->ranges[i].first);
-  ORCA_CHECK_ARG(items <= c->max_items, "batch needs %lld attention work items, the workspace "
-                 "holds %lld", (long long)items, (long long)c->max_items);
+  ORCA_CHECK_ARG(items <= c->max_items && pf <= c->max_pf, "batch needs %lld + %lld attention "
+                 "work items, the workspace holds %lld + %lld", (long long)items, (long long)pf,
+                 (long long)c->max_items, (long long)c->max_pf);
   *rows_out = int32_t(off);
   *items_out = items;
+  *pf_out = pf;
   return ORCA_OK;
 }
 
 // Lays the plan out in `buf` (packed, 16-byte aligned sections).
 void build_plan(const orca_ctx* c, const orca_req_desc* reqs, int32_t n, int32_t rows,
-                int64_t n_items, char* buf, Plan& p) {
+                int64_t n_items, int64_t n_pf, char* buf, Plan& p) {
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -143,23 +151,28 @@ void build_plan(const orca_ctx* c, const orca_req_desc* reqs, int32_t n, int32_t
   p.off_row_dst = take(sizeof(int32_t) * rows);
   p.off_items = take(sizeof(SplitItem) * n_items);
   p.off_srows = take(sizeof(SplitRow) * rows);
-  p.off_pf = 0;
+  p.off_pf = take(sizeof(PrefillItem) * n_pf);
   p.bytes = o;
   p.reqs = reinterpret_cast<DevReq*>(buf + p.off_reqs);
   p.row_dst = reinterpret_cast<int32_t*>(buf + p.off_row_dst);
   p.items = reinterpret_cast<SplitItem*>(buf + p.off_items);
   p.srows = reinterpret_cast<SplitRow*>(buf + p.off_srows);
-  p.pf = nullptr;
+  p.pf = reinterpret_cast<PrefillItem*>(buf + p.off_pf);
   p.n_reqs = n;
   p.rows = rows;
-  int ni = 0, ns = 0;
+  int ni = 0, ns = 0, np = 0;
   for (int i = 0; i < n; ++i) {
     const orca_req_desc& r = reqs[i];
     p.reqs[i] = DevReq{r.q_offset, r.q_len, r.kv_len, r.phase, r.kv_base};
+    const bool pre = uses_prefill(c, r);
+    if (pre)
+      for (int q0 = 0; q0 < r.q_len; q0 += PREFILL_ROWS)
+        p.pf[np++] = PrefillItem{i, q0, std::min(r.q_len, q0 + PREFILL_ROWS), 0};
     for (int j = 0; j < r.q_len; ++j) {
       const int row = r.q_offset + j;
       const int64_t pos = int64_t(r.kv_len) + j;
       p.row_dst[row] = int32_t(r.kv_base + pos);
+      if (pre) continue;
       const int keys = int(pos + 1);
       const int chunks = int(ceil_div(keys, SPLIT_CHUNK));
       p.srows[ns++] = SplitRow{row, ni, chunks, i};
@@ -169,7 +182,7 @@ void build_plan(const orca_ctx* c, const orca_req_desc* reqs, int32_t n, int32_t
   }
   p.n_items = ni;
   p.n_srows = ns;
-  (void)c;
+  p.n_pf = np;
 }
 
 orca_status hip_fail(hipError_t e, const char* what) {
@@ -187,14 +200,14 @@ orca_status hip_fail(hipError_t e, const char* what) {
 orca_status stage(orca_ctx* c, const orca_req_desc* reqs, int32_t n, char* ws, hipStream_t s,
                   Plan& p, AttnArgs& aa) {
   int32_t rows = 0;
-  int64_t n_items = 0;
-  orca_status st = validate(c, reqs, n, &rows, &n_items);
+  int64_t n_items = 0, n_pf = 0;
+  orca_status st = validate(c, reqs, n, &rows, &n_items, &n_pf);
   if (st != ORCA_OK) return st;
   const int slot = c->slot;
   c->slot = (c->slot + 1) % NSLOT;
   if (c->ev_live[slot]) HIP_TRY(hipEventSynchronize(c->ev[slot]), "metadata ring wait");
   char* host = static_cast<char*>(c->staging[slot]);
-  build_plan(c, reqs, n, rows, n_items, host, p);
+  build_plan(c, reqs, n, rows, n_items, n_pf, host, p);
   char* dev = ws + c->off_meta;
   if (p.bytes > 0) {
     HIP_TRY(hipMemcpyAsync(dev, host, p.bytes, hipMemcpyHostToDevice, s), "metadata upload");
@@ -213,8 +226,8 @@ orca_status stage(orca_ctx* c, const orca_req_desc* reqs, int32_t n, char* ws, h
   aa.n_items = p.n_items;
   aa.srows = reinterpret_cast<const SplitRow*>(dev + p.off_srows);
   aa.n_srows = p.n_srows;
-  aa.pf = nullptr;
-  aa.n_pf = 0;
+  aa.pf = reinterpret_cast<const PrefillItem*>(dev + p.off_pf);
+  aa.n_pf = p.n_pf;
   aa.part_o = reinterpret_cast<float*>(ws + c->off_part_o);
   aa.part_ml = reinterpret_cast<float*>(ws + c->off_part_ml);
   return ORCA_OK;
@@ -260,11 +273,12 @@ orca_status orca_create(const orca_model_desc* desc, const orca_layer_weights* l
   c->kv = kv;
   c->max_rows = max_rows;
   c->max_reqs = max_reqs;
-  // every row yields at most 1 + keys / SPLIT_CHUNK items; increment keys
-  // lie in disjoint pool ranges; initiation rows of one prompt add a
-  // triangle (bounded by max_rows^2 / 2)
-  c->max_items = int64_t(max_rows) + d.kv_capacity / SPLIT_CHUNK + 1 +
-                 (int64_t(max_rows) * max_rows / 2) / SPLIT_CHUNK + max_rows;
+  // split-KV items: every row yields at most 1 + keys / SPLIT_CHUNK; the
+  // keys of increment rows lie in disjoint pool ranges; fp32 initiation
+  // rows of one prompt add a triangle (bounded by max_rows^2 / 2)
+  c->max_items = int64_t(max_rows) + d.kv_capacity / SPLIT_CHUNK + 1;
+  if (d.dtype == ORCA_F32) c->max_items += (int64_t(max_rows) * max_rows / 2) / SPLIT_CHUNK + max_rows;
+  c->max_pf = d.dtype == ORCA_BF16 ? int64_t(max_rows) / PREFILL_ROWS + max_reqs : 0;
   const size_t R = max_rows, H = d.hidden, F = d.ffn, s = dsize(d.dtype);
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -280,7 +294,8 @@ orca_status orca_create(const orca_model_desc* desc, const orca_layer_weights* l
   c->off_part_o = take(size_t(c->max_items) * H * 4);
   c->off_part_ml = take(size_t(c->max_items) * d.heads * 2 * 4);
   c->meta_bytes = sizeof(DevReq) * max_reqs + sizeof(int32_t) * R +
-                  sizeof(SplitItem) * c->max_items + sizeof(SplitRow) * R + 16 * 8;
+                  sizeof(SplitItem) * c->max_items + sizeof(SplitRow) * R +
+                  sizeof(PrefillItem) * c->max_pf + 16 * 8;
   c->off_meta = take(c->meta_bytes);
   c->ws_bytes = o;
   hipError_t e = hipGetDevice(&c->device);

@@ -23,6 +23,10 @@
 //
 // fp32 path: a plain LDS-tiled FMA kernel (64 x 64 tile) for fp32 models.
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <type_traits>
 
 #include "device.h"
 #include "kernels.h"
@@ -37,141 +41,178 @@ struct EpiParams {
 };
 
 __device__ __forceinline__ float gelu_tanh(float v) {
-  // 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))  (Hendrycks & Gimpel)
+  // 0.5 v (1 + tanh(u)), u = sqrt(2/pi) (v + 0.044715 v^3)  (Hendrycks &
+  // Gimpel); 1 + tanh(u) = 2 - 2 / (exp(2u) + 1), exact at both limits.
   const float k0 = 0.7978845608028654f;
-  return 0.5f * v * (1.f + tanhf(k0 * (v + 0.044715f * v * v * v)));
+  const float u = k0 * (v + 0.044715f * v * v * v);
+  return v * (1.f - 1.f / (__expf(2.f * u) + 1.f));
 }
 
+// One output column of a Linear layer, fixed per lane before the epilogue:
+// where element (m, n) goes is col.ptr + m * col.stride, or for the K/V
+// blocks of the QKV projection col.ptr + row_dst[m] * d (the pool slot).
 template <typename T, int EPI>
-__device__ __forceinline__ void epi_store(const EpiParams& ep, int m, int n, float v) {
-  if constexpr (EPI == ORCA_EPI_BIAS) {
-    store_f32((T*)ep.out + (size_t)m * ep.ldo + n, v);
-  } else if constexpr (EPI == ORCA_EPI_BIAS_GELU) {
-    store_f32((T*)ep.out + (size_t)m * ep.ldo + n, gelu_tanh(v));
-  } else if constexpr (EPI == ORCA_EPI_BIAS_RESID) {
-    float* o = (float*)ep.out + (size_t)m * ep.ldo + n;
-    *o += v;
-  } else {
-    const int H = ep.qkv.hidden;
-    if (n < H) {
-      store_f32((T*)ep.qkv.q_out + (size_t)m * H + n, v);
-    } else {
-      int c = n - H;
-      T* pool = (T*)ep.qkv.k_pool;
-      if (c >= H) {
-        c -= H;
-        pool = (T*)ep.qkv.v_pool;
+struct EpiCol {
+  T* ptr;
+  size_t stride;
+  bool slot;      // indexed by the row's pool slot instead of the row
+  __device__ __forceinline__ EpiCol(const EpiParams& ep, int n) {
+    slot = false;
+    if constexpr (EPI == EPI_QKV) {
+      const int H = ep.qkv.hidden, d = ep.qkv.head_dim;
+      if (n < H) {
+        ptr = (T*)ep.qkv.q_out + n;
+        stride = H;
+      } else {
+        int c = n - H;
+        T* pool = (T*)ep.qkv.k_pool;
+        if (c >= H) {
+          c -= H;
+          pool = (T*)ep.qkv.v_pool;
+        }
+        const int h = c / d, dd = c - h * d;
+        ptr = pool + (size_t)h * ep.qkv.cap * d + dd;
+        stride = d;
+        slot = true;
       }
-      const int d = ep.qkv.head_dim;
-      const int h = c / d, dd = c - h * d;
-      store_f32(pool + ((size_t)h * ep.qkv.cap + ep.qkv.row_dst[m]) * d + dd, v);
+    } else {
+      ptr = (T*)ep.out + n;
+      stride = ep.ldo;
     }
   }
-}
+  // `row` is m, `dst` its pool slot (QKV only)
+  __device__ __forceinline__ void store(int row, int dst, float v) const {
+    T* p = ptr + (size_t)(slot ? dst : row) * stride;
+    if constexpr (EPI == ORCA_EPI_BIAS || EPI == EPI_QKV) {
+      store_f32(p, v);
+    } else if constexpr (EPI == ORCA_EPI_BIAS_GELU) {
+      store_f32(p, gelu_tanh(v));
+    } else {
+      *reinterpret_cast<float*>(p) += v;
+    }
+  }
+};
 
 // ---------------------------------------------------------------- bf16 MFMA
 
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
+constexpr int BK = 64, LDK = BK + 8;
 
 __device__ __forceinline__ int xcd_remap(int b, int nblk) {
   const int q = nblk / 8, r = nblk % 8, xcd = b % 8, local = b / 8;
   return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restrict__ A,
-                                                            const bf16* __restrict__ W,
-                                                            const bf16* __restrict__ bias,
-                                                            EpiParams ep, int M, int N, int K,
-                                                            int tiles_m) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDK];
+// Workgroup tile (64*TI) x (64*TJ): four waves in a 2 x 2 grid, each owning
+// (32*TI) x (32*TJ) outputs as TI x TJ 32x32 MFMA accumulators.
+template <int TI, int TJ>
+struct TileCfg {
+  static constexpr int BM = 64 * TI, BN = 64 * TJ;
+  static constexpr int LA = BM * 8 / 256, LB = BN * 8 / 256;   // 16-byte loads per thread
+  static constexpr int LDS = 2 * (BM + BN) * LDK * 2;          // bytes, two stages
+};
+
+template <int EPI, int TI, int TJ>
+__global__ __launch_bounds__(256, (TI * TJ >= 8 ? 1 : 2)) void gemm_bf16_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ bias,
+    EpiParams ep, int M, int N, int K, int tiles_m) {
+  using C = TileCfg<TI, TJ>;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][C::BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][C::BN * LDK];
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int tm = logical % tiles_m, tn = logical / tiles_m;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  const bf16* gA[4];
-  const bf16* gB[4];
-  int soff[4];
+  const bf16* gA[C::LA];
+  const bf16* gB[C::LB];
+  int oA[C::LA], oB[C::LB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < C::LA; ++i) {
     const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-    const int am = min(tm * BM + row, M - 1), bn = min(tn * BN + row, N - 1);
-    gA[i] = A + (size_t)am * K + ch * 8;
-    gB[i] = W + (size_t)bn * K + ch * 8;
-    soff[i] = row * LDK + ch * 8;
+    gA[i] = A + (size_t)min(tm * C::BM + row, M - 1) * K + ch * 8;
+    oA[i] = row * LDK + ch * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < C::LB; ++i) {
+    const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
+    gB[i] = W + (size_t)min(tn * C::BN + row, N - 1) * K + ch * 8;
+    oB[i] = row * LDK + ch * 8;
   }
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 ra[4], rb[4];
+  uint4 ra[C::LA], rb[C::LB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = *reinterpret_cast<const uint4*>(gA[i]);
-    rb[i] = *reinterpret_cast<const uint4*>(gB[i]);
-  }
+  for (int i = 0; i < C::LA; ++i) ra[i] = *reinterpret_cast<const uint4*>(gA[i]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    *reinterpret_cast<uint4*>(&sA[0][soff[i]]) = ra[i];
-    *reinterpret_cast<uint4*>(&sB[0][soff[i]]) = rb[i];
-  }
+  for (int i = 0; i < C::LB; ++i) rb[i] = *reinterpret_cast<const uint4*>(gB[i]);
+#pragma unroll
+  for (int i = 0; i < C::LA; ++i) *reinterpret_cast<uint4*>(&sA[0][oA[i]]) = ra[i];
+#pragma unroll
+  for (int i = 0; i < C::LB; ++i) *reinterpret_cast<uint4*>(&sB[0][oB[i]]) = rb[i];
   __syncthreads();
 
   const int KT = K / BK;
   const int fr = lane & 31, fk = (lane >> 5) * 8;
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) {
+    // prefetch the next K step (the last trip re-reads the current one, so
+    // the staging registers never sit behind a branch)
+    const int kn = min(kt + 1, KT - 1) * BK;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = *reinterpret_cast<const uint4*>(gA[i] + (kt + 1) * BK);
-        rb[i] = *reinterpret_cast<const uint4*>(gB[i] + (kt + 1) * BK);
-      }
-    }
-    const uint16_t* a_base = &sA[cur][(wm * 64 + fr) * LDK + fk];
-    const uint16_t* b_base = &sB[cur][(wn * 64 + fr) * LDK + fk];
+    for (int i = 0; i < C::LA; ++i) ra[i] = *reinterpret_cast<const uint4*>(gA[i] + kn);
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) rb[i] = *reinterpret_cast<const uint4*>(gB[i] + kn);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* a_base = &sA[cur][(wm * 32 * TI + fr) * LDK + fk];
+    const uint16_t* b_base = &sB[cur][(wn * 32 * TJ + fr) * LDK + fk];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(a_base + ks * 16);
-      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(a_base + 32 * LDK + ks * 16);
-      const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(b_base + ks * 16);
-      const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(b_base + 32 * LDK + ks * 16);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
-    }
-    if (kt + 1 < KT) {
+      bf16x8_t a[TI], b[TJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint4*>(&sA[cur ^ 1][soff[i]]) = ra[i];
-        *reinterpret_cast<uint4*>(&sB[cur ^ 1][soff[i]]) = rb[i];
-      }
+      for (int i = 0; i < TI; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(a_base + i * 32 * LDK + ks * 16);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        b[j] = *reinterpret_cast<const bf16x8_t*>(b_base + j * 32 * LDK + ks * 16);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
+#pragma unroll
+    for (int i = 0; i < C::LA; ++i) *reinterpret_cast<uint4*>(&sA[cur ^ 1][oA[i]]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) *reinterpret_cast<uint4*>(&sB[cur ^ 1][oB[i]]) = rb[i];
     __syncthreads();
   }
 
   // 32x32 accumulator layout: lane holds column lane%32 and rows
   // 8*(r/4) + 4*(lane/32) + r%4 for its 16 registers r.
+  using OutT = typename std::conditional<EPI == ORCA_EPI_BIAS_RESID, float, bf16>::type;
+  float bn[TJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = tn * BN + wn * 64 + j * 32 + fr;
+  for (int j = 0; j < TJ; ++j)
+    bn[j] = load_f32(bias + min(tn * C::BN + wn * 32 * TJ + j * 32 + fr, N - 1));
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int n = tn * C::BN + wn * 32 * TJ + j * 32 + fr;
     if (n >= N) continue;
-    const float bn = load_f32(bias + n);
+    const EpiCol<OutT, EPI> col(ep, n);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < TI; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = tm * BM + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m < M) epi_store<bf16, EPI>(ep, m, n, acc[i][j][r] + bn);
+        const int m = tm * C::BM + wm * 32 * TI + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m < M) col.store(m, EPI == EPI_QKV ? ep.qkv.row_dst[m] : 0, acc[i][j][r] + bn[j]);
       }
     }
   }
@@ -216,24 +257,55 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   for (int j = 0; j < 4; ++j) {
     const int n = tn * 64 + tx * 4 + j;
     if (n >= N) continue;
-    const float bv = bias[n];
+    const EpiCol<float, EPI> col(ep, n);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = tm * 64 + ty * 4 + i;
-      if (m < M) epi_store<float, EPI>(ep, m, n, acc[i][j] + bv);
+      if (m < M) col.store(m, EPI == EPI_QKV ? ep.qkv.row_dst[m] : 0, acc[i][j] + bias[n]);
     }
   }
 }
 
 // ---------------------------------------------------------------- launcher
 
+// Tile shape for an M x N output: the largest tiles keep the MFMAs busiest
+// per LDS byte; smaller ones are taken when the large ones leave most of the
+// 256 CUs idle in the last round of workgroups.
+struct TileChoice {
+  int ti, tj;
+};
+static TileChoice choose_tiles(int m, int n) {
+  // ORCA_GEMM_TILES=44|42|22 pins the tile shape (tests and tuning runs)
+  if (const char* f = getenv("ORCA_GEMM_TILES")) {
+    if (!strcmp(f, "44")) return {4, 4};
+    if (!strcmp(f, "42")) return {4, 2};
+    if (!strcmp(f, "22")) return {2, 2};
+  }
+  // measured on MI355X at the 13B and 175B layer shapes: the 128 x 128 tile
+  // with two workgroups per CU outruns the larger tiles (one wave per SIMD
+  // cannot hide the global-load latency of a K step)
+  (void)m;
+  (void)n;
+  return {2, 2};
+}
+
+template <int EPI, int TI, int TJ>
+static void launch_mfma(const void* a, const void* w, const void* bias, const EpiParams& ep, int m,
+                        int n, int k, hipStream_t s) {
+  using C = TileCfg<TI, TJ>;
+  const int tiles_m = (m + C::BM - 1) / C::BM, tiles_n = (n + C::BN - 1) / C::BN;
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, TI, TJ>), dim3(tiles_m * tiles_n), dim3(256), 0, s,
+                     (const bf16*)a, (const bf16*)w, (const bf16*)bias, ep, m, n, k, tiles_m);
+}
+
 template <int EPI>
 static void launch_typed(int dtype, const void* a, const void* w, const void* bias,
                          const EpiParams& ep, int m, int n, int k, hipStream_t s) {
   if (dtype == ORCA_BF16) {
-    const int tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
-    hipLaunchKernelGGL(gemm_bf16_kernel<EPI>, dim3(tiles_m * tiles_n), dim3(256), 0, s,
-                       (const bf16*)a, (const bf16*)w, (const bf16*)bias, ep, m, n, k, tiles_m);
+    const TileChoice t = choose_tiles(m, n);
+    if (t.ti == 4 && t.tj == 4) launch_mfma<EPI, 4, 4>(a, w, bias, ep, m, n, k, s);
+    else if (t.ti == 4) launch_mfma<EPI, 4, 2>(a, w, bias, ep, m, n, k, s);
+    else launch_mfma<EPI, 2, 2>(a, w, bias, ep, m, n, k, s);
   } else {
     hipLaunchKernelGGL(gemm_f32_kernel<EPI>, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, s,
                        (const float*)a, (const float*)w, (const float*)bias, ep, m, n, k);

@@ -64,8 +64,8 @@ struct AttnArgs {
 
 // Keys per split-KV work item for increment rows.
 constexpr int SPLIT_CHUNK = 512;
-// Query rows per prefill tile.
-constexpr int PREFILL_ROWS = 64;
+// Query positions per prefill (initiation) workgroup.
+constexpr int PREFILL_ROWS = 128;
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

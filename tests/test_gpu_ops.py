@@ -129,7 +129,7 @@ def test_qkv_split_and_append(dtype, m, hidden, heads):
 
 ATTN_CASES = [
     # dtype, hidden, heads, [(q_len, kv_len) ...]
-    ("bf16", 512, 4, [(1, 1), (1, 5), (1, 511), (1, 512), (1, 513), (1, 1100), (1, 2047),
+    ("bf16", 512, 4, [(1, 1), (1, 5), (1, 511), (1, 512), (1, 513), (1, 1100), (1, 2047), (517, 0),
                       (1, 2048), (1, 4200), (1, 0), (2, 0), (63, 0), (64, 0), (65, 0), (200, 0)]),
     ("bf16", 512, 8, [(1, 3), (1, 700), (1, 1500), (37, 0), (129, 0), (1, 0)]),
     ("f32", 64, 4, [(1, 3), (1, 4), (2, 0), (3, 0)]),
