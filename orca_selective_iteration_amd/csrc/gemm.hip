@@ -11,8 +11,8 @@
 // arithmetic.  0h-n0.github.io digest, implementation notes: fused GeLU.
 //
 // bf16 path: MFMA (v_mfma_f32_32x32x16_bf16) with fp32 accumulation.
-// Workgroup tile 128 x 128, K step 64, four waves each owning 64 x 64 of the
-// output (2 x 2 MFMA tiles).  Both operands are K-contiguous in HBM (A is
+// Workgroup tiles of 256 x 256 (eight waves, each 64 x 128) or 128 x 128
+// (four waves, each 64 x 64), K step 64.  Both operands are K-contiguous in HBM (A is
 // [M][K], W is [N][K]), loaded with 16-byte coalesced loads into registers,
 // then into a double-buffered LDS stage padded by 16 bytes per row so the
 // 16-byte fragment reads of a wave hit distinct banks.  One barrier per K
@@ -102,40 +102,42 @@ __device__ __forceinline__ int xcd_remap(int b, int nblk) {
   return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
-// Workgroup tile (64*TI) x (64*TJ): four waves in a 2 x 2 grid, each owning
-// (32*TI) x (32*TJ) outputs as TI x TJ 32x32 MFMA accumulators.
-template <int TI, int TJ>
+// Workgroup tile (WGM*32*TI) x (WGN*32*TJ): a WGM x WGN grid of waves, each
+// owning (32*TI) x (32*TJ) outputs as TI x TJ 32x32 MFMA accumulators.
+template <int WGM, int WGN, int TI, int TJ>
 struct TileCfg {
-  static constexpr int BM = 64 * TI, BN = 64 * TJ;
-  static constexpr int LA = BM * 8 / 256, LB = BN * 8 / 256;   // 16-byte loads per thread
-  static constexpr int LDS = 2 * (BM + BN) * LDK * 2;          // bytes, two stages
+  static constexpr int NT = 64 * WGM * WGN;                    // threads
+  static constexpr int BM = WGM * 32 * TI, BN = WGN * 32 * TJ;
+  static constexpr int LA = BM * 8 / NT, LB = BN * 8 / NT;     // 16-byte loads per thread
+  static_assert(LA * NT == BM * 8 && LB * NT == BN * 8, "tile not divisible by threads");
 };
 
-template <int EPI, int TI, int TJ>
-__global__ __launch_bounds__(256, (TI * TJ >= 8 ? 1 : 2)) void gemm_bf16_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ bias,
-    EpiParams ep, int M, int N, int K, int tiles_m) {
-  using C = TileCfg<TI, TJ>;
+template <int EPI, int WGM, int WGN, int TI, int TJ>
+__global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && TI * TJ <= 4) ? 2 : 1)
+void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
+                      const bf16* __restrict__ bias, EpiParams ep, int M, int N, int K,
+                      int tiles_m) {
+  using C = TileCfg<WGM, WGN, TI, TJ>;
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][C::BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][C::BN * LDK];
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int tm = logical % tiles_m, tn = logical / tiles_m;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   const bf16* gA[C::LA];
   const bf16* gB[C::LB];
   int oA[C::LA], oB[C::LB];
 #pragma unroll
   for (int i = 0; i < C::LA; ++i) {
-    const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
+    const int c = tid + C::NT * i, row = c >> 3, ch = c & 7;
     gA[i] = A + (size_t)min(tm * C::BM + row, M - 1) * K + ch * 8;
     oA[i] = row * LDK + ch * 8;
   }
 #pragma unroll
   for (int i = 0; i < C::LB; ++i) {
-    const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
+    const int c = tid + C::NT * i, row = c >> 3, ch = c & 7;
     gB[i] = W + (size_t)min(tn * C::BN + row, N - 1) * K + ch * 8;
     oB[i] = row * LDK + ch * 8;
   }
@@ -268,44 +270,48 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 // ---------------------------------------------------------------- launcher
 
-// Tile shape for an M x N output: the largest tiles keep the MFMAs busiest
-// per LDS byte; smaller ones are taken when the large ones leave most of the
-// 256 CUs idle in the last round of workgroups.
-struct TileChoice {
-  int ti, tj;
-};
-static TileChoice choose_tiles(int m, int n) {
-  // ORCA_GEMM_TILES=44|42|22 pins the tile shape (tests and tuning runs)
-  if (const char* f = getenv("ORCA_GEMM_TILES")) {
-    if (!strcmp(f, "44")) return {4, 4};
-    if (!strcmp(f, "42")) return {4, 2};
-    if (!strcmp(f, "22")) return {2, 2};
+// Tile shape for an M x N output.  Variants (wave grid x per-wave tiles):
+//   0: 2x2 waves, 2x2 tiles -> 128 x 128, 256 threads, 2 workgroups / CU
+//   1: 2x2 waves, 4x4 tiles -> 256 x 256, 256 threads
+//   2: 2x4 waves, 4x2 tiles -> 256 x 256, 512 threads
+//   3: 4x2 waves, 2x4 tiles -> 256 x 256, 512 threads
+//   4: 2x4 waves, 2x2 tiles -> 128 x 256, 512 threads
+//   5: 4x2 waves, 2x2 tiles -> 256 x 128, 512 threads
+// ORCA_GEMM_VARIANT=<n> pins the variant (tests and tuning runs).
+static int choose_variant(int m, int n) {
+  if (const char* f = getenv("ORCA_GEMM_VARIANT")) {
+    const int v = atoi(f);
+    if (v >= 0 && v <= 5) return v;
   }
-  // measured on MI355X at the 13B and 175B layer shapes: the 128 x 128 tile
-  // with two workgroups per CU outruns the larger tiles (one wave per SIMD
-  // cannot hide the global-load latency of a K step)
-  (void)m;
-  (void)n;
-  return {2, 2};
+  // measured on MI355X at the 13B / 175B layer shapes: the 8-wave 256 x 256
+  // tile (variant 3) is fastest once it yields enough tiles to spread over
+  // the 256 CUs; below that the 128 x 128 tile keeps more CUs busy
+  const long big = (long)((m + 255) / 256) * ((n + 255) / 256);
+  return big >= 128 ? 3 : 0;
 }
 
-template <int EPI, int TI, int TJ>
+template <int EPI, int WGM, int WGN, int TI, int TJ>
 static void launch_mfma(const void* a, const void* w, const void* bias, const EpiParams& ep, int m,
                         int n, int k, hipStream_t s) {
-  using C = TileCfg<TI, TJ>;
+  using C = TileCfg<WGM, WGN, TI, TJ>;
   const int tiles_m = (m + C::BM - 1) / C::BM, tiles_n = (n + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, TI, TJ>), dim3(tiles_m * tiles_n), dim3(256), 0, s,
-                     (const bf16*)a, (const bf16*)w, (const bf16*)bias, ep, m, n, k, tiles_m);
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WGM, WGN, TI, TJ>), dim3(tiles_m * tiles_n),
+                     dim3(C::NT), 0, s, (const bf16*)a, (const bf16*)w, (const bf16*)bias, ep, m,
+                     n, k, tiles_m);
 }
 
 template <int EPI>
 static void launch_typed(int dtype, const void* a, const void* w, const void* bias,
                          const EpiParams& ep, int m, int n, int k, hipStream_t s) {
   if (dtype == ORCA_BF16) {
-    const TileChoice t = choose_tiles(m, n);
-    if (t.ti == 4 && t.tj == 4) launch_mfma<EPI, 4, 4>(a, w, bias, ep, m, n, k, s);
-    else if (t.ti == 4) launch_mfma<EPI, 4, 2>(a, w, bias, ep, m, n, k, s);
-    else launch_mfma<EPI, 2, 2>(a, w, bias, ep, m, n, k, s);
+    switch (choose_variant(m, n)) {
+      case 1: launch_mfma<EPI, 2, 2, 4, 4>(a, w, bias, ep, m, n, k, s); break;
+      case 2: launch_mfma<EPI, 2, 4, 4, 2>(a, w, bias, ep, m, n, k, s); break;
+      case 3: launch_mfma<EPI, 4, 2, 2, 4>(a, w, bias, ep, m, n, k, s); break;
+      case 4: launch_mfma<EPI, 2, 4, 2, 2>(a, w, bias, ep, m, n, k, s); break;
+      case 5: launch_mfma<EPI, 4, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;
+      default: launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;
+    }
   } else {
     hipLaunchKernelGGL(gemm_f32_kernel<EPI>, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, s,
                        (const float*)a, (const float*)w, (const float*)bias, ep, m, n, k);
