@@ -112,7 +112,7 @@ struct TileCfg {
   static_assert(LA * NT == BM * 8 && LB * NT == BN * 8, "tile not divisible by threads");
 };
 
-template <int EPI, int WGM, int WGN, int TI, int TJ>
+template <int EPI, int WGM, int WGN, int TI, int TJ, bool PIPE>
 __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && TI * TJ <= 4) ? 2 : 1)
 void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
                       const bf16* __restrict__ bias, EpiParams ep, int M, int N, int K,
@@ -163,38 +163,101 @@ void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
 
   const int KT = K / BK;
   const int fr = lane & 31, fk = (lane >> 5) * 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    // prefetch the next K step (the last trip re-reads the current one, so
-    // the staging registers never sit behind a branch)
-    const int kn = min(kt + 1, KT - 1) * BK;
+  const int a_off = (wm * 32 * TI + fr) * LDK + fk, b_off = (wn * 32 * TJ + fr) * LDK + fk;
+  if constexpr (!PIPE) {
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = kt & 1;
+      // prefetch the next K step (the last trip re-reads the current one, so
+      // the staging registers never sit behind a branch)
+      const int kn = min(kt + 1, KT - 1) * BK;
 #pragma unroll
-    for (int i = 0; i < C::LA; ++i) ra[i] = *reinterpret_cast<const uint4*>(gA[i] + kn);
+      for (int i = 0; i < C::LA; ++i) ra[i] = *reinterpret_cast<const uint4*>(gA[i] + kn);
 #pragma unroll
-    for (int i = 0; i < C::LB; ++i) rb[i] = *reinterpret_cast<const uint4*>(gB[i] + kn);
-    __builtin_amdgcn_sched_barrier(0);
-    const uint16_t* a_base = &sA[cur][(wm * 32 * TI + fr) * LDK + fk];
-    const uint16_t* b_base = &sB[cur][(wn * 32 * TJ + fr) * LDK + fk];
+      for (int i = 0; i < C::LB; ++i) rb[i] = *reinterpret_cast<const uint4*>(gB[i] + kn);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t* a_base = &sA[cur][a_off];
+      const uint16_t* b_base = &sB[cur][b_off];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t a[TI], b[TJ];
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        bf16x8_t a[TI], b[TJ];
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(a_base + i * 32 * LDK + ks * 16);
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(b_base + j * 32 * LDK + ks * 16);
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
+        for (int i = 0; i < TI; ++i)
+          a[i] = *reinterpret_cast<const bf16x8_t*>(a_base + i * 32 * LDK + ks * 16);
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          b[j] = *reinterpret_cast<const bf16x8_t*>(b_base + j * 32 * LDK + ks * 16);
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < C::LA; ++i) *reinterpret_cast<uint4*>(&sA[cur ^ 1][oA[i]]) = ra[i];
+#pragma unroll
+      for (int i = 0; i < C::LB; ++i) *reinterpret_cast<uint4*>(&sB[cur ^ 1][oB[i]]) = rb[i];
+      __syncthreads();
     }
+  } else {
+    // Fragments of K sub-step ks+1 are read from LDS while the MFMAs of ks
+    // run; the fragments of the next K step's first sub-step are read right
+    // after the barrier that publishes it.
+    bf16x8_t fa[2][TI], fb[2][TJ];
 #pragma unroll
-    for (int i = 0; i < C::LA; ++i) *reinterpret_cast<uint4*>(&sA[cur ^ 1][oA[i]]) = ra[i];
+    for (int i = 0; i < TI; ++i)
+      fa[0][i] = *reinterpret_cast<const bf16x8_t*>(&sA[0][a_off + i * 32 * LDK]);
 #pragma unroll
-    for (int i = 0; i < C::LB; ++i) *reinterpret_cast<uint4*>(&sB[cur ^ 1][oB[i]]) = rb[i];
-    __syncthreads();
+    for (int j = 0; j < TJ; ++j)
+      fb[0][j] = *reinterpret_cast<const bf16x8_t*>(&sB[0][b_off + j * 32 * LDK]);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = kt & 1;
+      const int kn = min(kt + 1, KT - 1) * BK;
+#pragma unroll
+      for (int i = 0; i < C::LA; ++i) ra[i] = *reinterpret_cast<const uint4*>(gA[i] + kn);
+#pragma unroll
+      for (int i = 0; i < C::LB; ++i) rb[i] = *reinterpret_cast<const uint4*>(gB[i] + kn);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t* a_base = &sA[cur][a_off];
+      const uint16_t* b_base = &sB[cur][b_off];
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int f = ks & 1;
+        if (ks + 1 < BK / 16) {
+#pragma unroll
+          for (int i = 0; i < TI; ++i)
+            fa[f ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(a_base + i * 32 * LDK + (ks + 1) * 16);
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            fb[f ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(b_base + j * 32 * LDK + (ks + 1) * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
+          }
+        // interleave: one fragment read between MFMAs
+        if (ks + 1 < BK / 16) {
+#pragma unroll
+          for (int q = 0; q < TI + TJ; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - TI - TJ, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < C::LA; ++i) *reinterpret_cast<uint4*>(&sA[cur ^ 1][oA[i]]) = ra[i];
+#pragma unroll
+      for (int i = 0; i < C::LB; ++i) *reinterpret_cast<uint4*>(&sB[cur ^ 1][oB[i]]) = rb[i];
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        fa[0][i] = *reinterpret_cast<const bf16x8_t*>(&sA[cur ^ 1][a_off + i * 32 * LDK]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        fb[0][j] = *reinterpret_cast<const bf16x8_t*>(&sB[cur ^ 1][b_off + j * 32 * LDK]);
+    }
   }
 
   // 32x32 accumulator layout: lane holds column lane%32 and rows
@@ -277,11 +340,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 //   3: 4x2 waves, 2x4 tiles -> 256 x 256, 512 threads
 //   4: 2x4 waves, 2x2 tiles -> 128 x 256, 512 threads
 //   5: 4x2 waves, 2x2 tiles -> 256 x 128, 512 threads
+//   6: as 3, with the LDS fragment reads software-pipelined
+//   7: as 0, with the LDS fragment reads software-pipelined
 // ORCA_GEMM_VARIANT=<n> pins the variant (tests and tuning runs).
 static int choose_variant(int m, int n) {
   if (const char* f = getenv("ORCA_GEMM_VARIANT")) {
     const int v = atoi(f);
-    if (v >= 0 && v <= 5) return v;
+    if (v >= 0 && v <= 7) return v;
   }
   // measured on MI355X at the 13B / 175B layer shapes: the 8-wave 256 x 256
   // tile (variant 3) is fastest once it yields enough tiles to spread over
@@ -290,12 +355,12 @@ static int choose_variant(int m, int n) {
   return big >= 128 ? 3 : 0;
 }
 
-template <int EPI, int WGM, int WGN, int TI, int TJ>
+template <int EPI, int WGM, int WGN, int TI, int TJ, bool PIPE = false>
 static void launch_mfma(const void* a, const void* w, const void* bias, const EpiParams& ep, int m,
                         int n, int k, hipStream_t s) {
   using C = TileCfg<WGM, WGN, TI, TJ>;
   const int tiles_m = (m + C::BM - 1) / C::BM, tiles_n = (n + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WGM, WGN, TI, TJ>), dim3(tiles_m * tiles_n),
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WGM, WGN, TI, TJ, PIPE>), dim3(tiles_m * tiles_n),
                      dim3(C::NT), 0, s, (const bf16*)a, (const bf16*)w, (const bf16*)bias, ep, m,
                      n, k, tiles_m);
 }
@@ -310,6 +375,8 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
       case 3: launch_mfma<EPI, 4, 2, 2, 4>(a, w, bias, ep, m, n, k, s); break;
       case 4: launch_mfma<EPI, 2, 4, 2, 2>(a, w, bias, ep, m, n, k, s); break;
       case 5: launch_mfma<EPI, 4, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;
+      case 6: launch_mfma<EPI, 4, 2, 2, 4, true>(a, w, bias, ep, m, n, k, s); break;
+      case 7: launch_mfma<EPI, 2, 2, 2, 2, true>(a, w, bias, ep, m, n, k, s); break;
       default: launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;
     }
   } else {

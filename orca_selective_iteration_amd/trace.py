@@ -1,0 +1,201 @@
+"""End-to-end iteration-level scheduling trace on one GPU.
+
+    python -m orca_selective_iteration_amd.trace [--requests 1000] [--rate 32]
+        [--workload gpt13b-40l] [--policy both|iteration|static] [--log FILE]
+
+Requests arrive as a seeded Poisson stream (prompt and output lengths
+uniform); the native scheduler (orca_sched_*) picks every iteration's batch
+(garden.houmin.site/infra/orca 3.1.1: evict finished requests, admit waiting
+ones FCFS within the batch, token and K/V budgets) and orca_iteration runs it.
+The clock is the wall clock of the serving loop: each step is taken at the
+time the previous iteration finished on the GPU (the engine hands back one
+token per request per iteration, so the loop waits for it).  The same trace
+runs under request-level (static) batching for comparison
+(0h-n0.github.io digest: a static batch lasts as long as its longest member).
+
+No embedding or LM head exists here: the hidden rows fed to every iteration
+are seeded N(0,1) rows, and a request's output length is fixed in advance
+(it plays the role of the end-of-sequence token).  The K/V pool is sized to
+the HBM left after the weights and the workspace; every cached entry is
+produced by the model's own initiation and increment iterations.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+import time
+from typing import List, Optional
+
+import numpy as np
+
+from . import lib as L
+from . import synth
+
+
+class TraceEngine:
+    """Weights, an HBM-sized K/V pool and one engine context."""
+
+    def __init__(self, work: synth.Workload, max_batch: int, token_budget: int,
+                 kv_slots: Optional[int] = None, hbm_fraction: float = 0.85, seed: int = 0,
+                 log=None):
+        import torch
+        log = log or (lambda *a: None)
+        self.work = work
+        self.tdt = torch.bfloat16 if work.dtype == "bf16" else torch.float32
+        self.odt = L.ORCA_BF16 if work.dtype == "bf16" else L.ORCA_F32
+        esz = 2 if work.dtype == "bf16" else 4
+        self.weights = [synth.device_param_tensors(work, seed * 1000003 + l, "cuda", self.tdt)
+                        for l in range(work.layers)]
+        self.max_rows = token_budget
+        self.max_reqs = max_batch
+        per_token = 2 * work.layers * work.hidden * esz
+        if kv_slots is None:
+            free, _ = torch.cuda.mem_get_info()
+            ws_guess = 64 * work.hidden * self.max_rows + 8 * work.ffn * self.max_rows
+            kv_slots = int((free * hbm_fraction - ws_guess) // per_token)
+        self.cap = int(kv_slots)
+        log(f"K/V pool: {self.cap} token slots ({self.cap * per_token / 1e9:.1f} GB)")
+        shape = (work.layers, work.heads, self.cap, work.head_dim)
+        self.k_pool = torch.empty(shape, dtype=self.tdt, device="cuda")
+        self.v_pool = torch.empty(shape, dtype=self.tdt, device="cuda")
+        self.kv = L.orca_kv_create(self.cap)
+        self.ctx = L.orca_create(work.layers, work.hidden, work.heads, work.ffn, self.odt,
+                                 work.eps, self.cap, self.weights, self.k_pool, self.v_pool,
+                                 self.kv, self.max_rows, self.max_reqs)
+        self.ws_bytes = L.orca_workspace_bytes(self.ctx)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.x = synth.device_normal_(torch.empty((self.max_rows, work.hidden), dtype=self.tdt,
+                                                  device="cuda"), seed * 17 + 3)
+        self.y = torch.empty_like(self.x)
+
+    def run(self, requests: List[synth.TraceRequest], max_batch: int, token_budget: int,
+            policy: int, log=None, max_wall: float = 1e9) -> dict:
+        import torch
+        log = log or (lambda *a: None)
+        s = L.orca_sched_create(self.kv, max_batch, token_budget, policy)
+        stream = torch.cuda.current_stream()
+        try:
+            for r in requests:
+                L.orca_sched_submit(s, r.id, r.arrival, r.prompt_len, r.max_tokens, r.out_len)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            now = 0.0
+            steps: List[tuple] = []      # non-empty iterations: (now, ids)
+            calls: List[tuple] = []      # every scheduling step, for replay
+            iters = rows = busy = 0
+            last_print = t0
+            while not L.orca_sched_idle(s):
+                descs, ids = L.orca_sched_step(s, now, max_batch)
+                calls.append((now, tuple(ids)))
+                if not descs:
+                    if L.orca_sched_idle(s):
+                        break
+                    nxt = L.orca_sched_next_arrival(s)
+                    if nxt is None:
+                        raise RuntimeError("scheduler idle with active requests")
+                    # nothing to run until the next arrival: wait for it
+                    time.sleep(max(0.0, nxt - (time.perf_counter() - t0)))
+                    now = max(time.perf_counter() - t0, nxt)
+                    continue
+                n_rows = descs[-1].q_offset + descs[-1].q_len
+                L.orca_iteration(self.ctx, descs, self.x, self.y, self.ws, self.ws_bytes, stream)
+                stream.synchronize()
+                steps.append((now, tuple(ids)))
+                iters += 1
+                rows += n_rows
+                busy += len(descs)
+                now = time.perf_counter() - t0
+                if now > max_wall:
+                    raise RuntimeError(f"trace exceeded {max_wall} s")
+                if time.perf_counter() - last_print > 20:
+                    log(f"  t={now:.1f}s iterations={iters} rows={rows}")
+                    last_print = time.perf_counter()
+            wall = time.perf_counter() - t0
+            # per-request latency: time the iteration holding its last token ended
+            iter_end = [steps[k + 1][0] if k + 1 < len(steps) else wall for k in range(len(steps))]
+            lats = []
+            for r in requests:
+                adm, fin, _ = L.orca_sched_request_info(s, r.id)
+                if policy == L.ORCA_POLICY_STATIC:
+                    # request-level: the response leaves with the whole batch
+                    _, _, rel = L.orca_sched_request_info(s, r.id)
+                    t_end = steps[rel][0] if rel < len(steps) else wall
+                else:
+                    t_end = iter_end[fin]
+                lats.append(t_end - r.arrival)
+            gen = sum(r.out_len for r in requests)
+            lats = np.array(lats)
+            return {
+                "policy": "iteration" if policy == L.ORCA_POLICY_ITERATION else "static",
+                "wall_s": round(wall, 3), "iterations": iters, "rows_processed": rows,
+                "generated_tokens": gen,
+                "generated_tokens_per_s": round(gen / wall, 1),
+                "processed_tokens_per_s": round(rows / wall, 1),
+                "requests_per_s": round(len(requests) / wall, 3),
+                "mean_batch": round(busy / max(iters, 1), 2),
+                "latency_s": {"mean": round(float(lats.mean()), 3),
+                              "p50": round(float(np.percentile(lats, 50)), 3),
+                              "p99": round(float(np.percentile(lats, 99)), 3)},
+                "steps": steps,
+                "calls": calls,
+            }
+        finally:
+            L.orca_sched_destroy(s)
+
+    def close(self):
+        if self.ctx:
+            L.orca_destroy(self.ctx)
+            self.ctx = None
+        if self.kv:
+            L.orca_kv_destroy(self.kv)
+            self.kv = None
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    p.add_argument("--workload", default="gpt13b-40l")
+    p.add_argument("--requests", type=int, default=1000)
+    p.add_argument("--rate", type=float, default=32.0, help="arrivals per second (inf: all at 0)")
+    p.add_argument("--max-batch", type=int, default=64)
+    p.add_argument("--token-budget", type=int, default=4096)
+    p.add_argument("--policy", choices=["both", "iteration", "static"], default="both")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--log", default=None, help="write the per-step (now, ids) log as JSON")
+    p.add_argument("--max-wall", type=float, default=600.0)
+    a = p.parse_args(argv)
+    import torch
+    log = lambda *m: print(*m, file=sys.stderr, flush=True)
+    work = synth.workload(a.workload, a.seed)
+    reqs = synth.poisson_trace(a.requests, a.rate, a.seed)
+    eng = TraceEngine(work, a.max_batch, a.token_budget, seed=a.seed, log=log)
+    out = {"workload": a.workload, "requests": a.requests, "rate": a.rate,
+           "max_batch": a.max_batch, "token_budget": a.token_budget, "kv_slots": eng.cap,
+           "runs": []}
+    try:
+        # warm the kernels once
+        warm = [synth.TraceRequest(10**9, 0.0, 64, 8, 2)]
+        eng.run(warm, a.max_batch, a.token_budget, L.ORCA_POLICY_ITERATION)
+        pols = {"both": [L.ORCA_POLICY_ITERATION, L.ORCA_POLICY_STATIC],
+                "iteration": [L.ORCA_POLICY_ITERATION], "static": [L.ORCA_POLICY_STATIC]}[a.policy]
+        for pol in pols:
+            log(f"policy {'iteration' if pol == 0 else 'static'}: {a.requests} requests at "
+                f"{a.rate}/s")
+            res = eng.run(reqs, a.max_batch, a.token_budget, pol, log=log, max_wall=a.max_wall)
+            res.pop("steps")
+            calls = res.pop("calls")
+            log(json.dumps(res))
+            res["log"] = calls if a.log else None
+            out["runs"].append(res)
+    finally:
+        eng.close()
+    if a.log:
+        with open(a.log, "w") as f:
+            json.dump(out, f)
+    for r in out["runs"]:
+        r.pop("log", None)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
