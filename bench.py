@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--kernel-reps", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["iteration", "gemm", "decode"], default=None,
+    p.add_argument("--only", choices=["iteration", "gemm", "decode", "copy"], default=None,
                    help="run one timed region only (for profiling)")
     return p.parse_args()
 
@@ -107,6 +107,16 @@ def main():
     from orca_selective_iteration_amd.runner import DeviceModel
 
     torch.cuda.set_device(0)
+    if args.only == "copy":
+        # reference for the profiler's byte counters: a plain device copy of
+        # exactly 1 GiB read + 1 GiB written per launch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.kernel_reps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.kernel_reps} x 1 GiB")
+        return
     work = synth.workload(args.workload, args.seed)
     t0 = time.time()
     host = synth.host_inputs(work, args.seed) if work.layers * work.hidden <= 4096 else None

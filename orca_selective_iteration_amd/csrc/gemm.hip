@@ -199,65 +199,59 @@ void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
       __syncthreads();
     }
   } else {
-    // Fragments of K sub-step ks+1 are read from LDS while the MFMAs of ks
-    // run; the fragments of the next K step's first sub-step are read right
-    // after the barrier that publishes it.
-    bf16x8_t fa[2][TI], fb[2][TJ];
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-      fa[0][i] = *reinterpret_cast<const bf16x8_t*>(&sA[0][a_off + i * 32 * LDK]);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-      fb[0][j] = *reinterpret_cast<const bf16x8_t*>(&sB[0][b_off + j * 32 * LDK]);
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      const int kn = min(kt + 1, KT - 1) * BK;
-#pragma unroll
-      for (int i = 0; i < C::LA; ++i) ra[i] = *reinterpret_cast<const uint4*>(gA[i] + kn);
-#pragma unroll
-      for (int i = 0; i < C::LB; ++i) rb[i] = *reinterpret_cast<const uint4*>(gB[i] + kn);
-      __builtin_amdgcn_sched_barrier(0);
-      const uint16_t* a_base = &sA[cur][a_off];
-      const uint16_t* b_base = &sB[cur][b_off];
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int f = ks & 1;
-        if (ks + 1 < BK / 16) {
-#pragma unroll
-          for (int i = 0; i < TI; ++i)
-            fa[f ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(a_base + i * 32 * LDK + (ks + 1) * 16);
-#pragma unroll
-          for (int j = 0; j < TJ; ++j)
-            fb[f ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(b_base + j * 32 * LDK + (ks + 1) * 16);
-        }
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
-          }
-        // interleave: one fragment read between MFMAs
-        if (ks + 1 < BK / 16) {
-#pragma unroll
-          for (int q = 0; q < TI + TJ; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - TI - TJ, 0);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < C::LA; ++i) *reinterpret_cast<uint4*>(&sA[cur ^ 1][oA[i]]) = ra[i];
-#pragma unroll
-      for (int i = 0; i < C::LB; ++i) *reinterpret_cast<uint4*>(&sB[cur ^ 1][oB[i]]) = rb[i];
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-        fa[0][i] = *reinterpret_cast<const bf16x8_t*>(&sA[cur ^ 1][a_off + i * 32 * LDK]);
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        fb[0][j] = *reinterpret_cast<const bf16x8_t*>(&sB[cur ^ 1][b_off + j * 32 * LDK]);
+    // Two K steps in flight: at step kt the loads of step kt+2 are issued
+    // into one register set while the other set (step kt+1, requested a
+    // whole step earlier) is written to the LDS buffer freed by step kt-1.
+    // The sets are vector values (not arrays) so they stay in registers.
+    typedef uint32_t StageA __attribute__((ext_vector_type(4 * C::LA)));
+    typedef uint32_t StageB __attribute__((ext_vector_type(4 * C::LB)));
+    StageA pa0, pa1;
+    StageB pb0, pb1;
+#define ORCA_LOAD_STAGE(PA, PB, KOFF)                                                        \
+  _Pragma("unroll") for (int i = 0; i < C::LA; ++i) {                                        \
+    const uint4 t = *reinterpret_cast<const uint4*>(gA[i] + (KOFF));                         \
+    PA[4 * i] = t.x; PA[4 * i + 1] = t.y; PA[4 * i + 2] = t.z; PA[4 * i + 3] = t.w;          \
+  }                                                                                          \
+  _Pragma("unroll") for (int i = 0; i < C::LB; ++i) {                                        \
+    const uint4 t = *reinterpret_cast<const uint4*>(gB[i] + (KOFF));                         \
+    PB[4 * i] = t.x; PB[4 * i + 1] = t.y; PB[4 * i + 2] = t.z; PB[4 * i + 3] = t.w;          \
+  }
+#define ORCA_STORE_STAGE(PA, PB, BUF)                                                        \
+  _Pragma("unroll") for (int i = 0; i < C::LA; ++i)                                          \
+      *reinterpret_cast<uint4*>(&sA[BUF][oA[i]]) =                                           \
+          make_uint4(PA[4 * i], PA[4 * i + 1], PA[4 * i + 2], PA[4 * i + 3]);                \
+  _Pragma("unroll") for (int i = 0; i < C::LB; ++i)                                          \
+      *reinterpret_cast<uint4*>(&sB[BUF][oB[i]]) =                                           \
+          make_uint4(PB[4 * i], PB[4 * i + 1], PB[4 * i + 2], PB[4 * i + 3]);
+#define ORCA_GEMM_STEP(KT_, LA_, LB_, WA_, WB_)                                              \
+  {                                                                                          \
+    const int cur = (KT_) & 1;                                                               \
+    ORCA_LOAD_STAGE(LA_, LB_, min((KT_) + 2, KT - 1) * BK)                                   \
+    ORCA_STORE_STAGE(WA_, WB_, cur ^ 1)                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                       \
+    const uint16_t* a_base = &sA[cur][a_off];                                                \
+    const uint16_t* b_base = &sB[cur][b_off];                                                \
+    _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks) {                                 \
+      bf16x8_t a[TI], b[TJ];                                                                 \
+      _Pragma("unroll") for (int i = 0; i < TI; ++i) a[i] =                                  \
+          *reinterpret_cast<const bf16x8_t*>(a_base + i * 32 * LDK + ks * 16);               \
+      _Pragma("unroll") for (int j = 0; j < TJ; ++j) b[j] =                                  \
+          *reinterpret_cast<const bf16x8_t*>(b_base + j * 32 * LDK + ks * 16);               \
+      _Pragma("unroll") for (int i = 0; i < TI; ++i)                                         \
+          _Pragma("unroll") for (int j = 0; j < TJ; ++j) acc[i][j] =                         \
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);       \
+    }                                                                                        \
+    __syncthreads();                                                                         \
+  }
+    ORCA_LOAD_STAGE(pa1, pb1, min(1, KT - 1) * BK)
+    // the launcher takes this path only for an even number of K steps
+    for (int kt = 0; kt < KT; kt += 2) {
+      ORCA_GEMM_STEP(kt, pa0, pb0, pa1, pb1)
+      ORCA_GEMM_STEP(kt + 1, pa1, pb1, pa0, pb0)
     }
+#undef ORCA_GEMM_STEP
+#undef ORCA_LOAD_STAGE
+#undef ORCA_STORE_STAGE
   }
 
   // 32x32 accumulator layout: lane holds column lane%32 and rows
@@ -340,8 +334,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 //   3: 4x2 waves, 2x4 tiles -> 256 x 256, 512 threads
 //   4: 2x4 waves, 2x2 tiles -> 128 x 256, 512 threads
 //   5: 4x2 waves, 2x2 tiles -> 256 x 128, 512 threads
-//   6: as 3, with the LDS fragment reads software-pipelined
-//   7: as 0, with the LDS fragment reads software-pipelined
+//   6: as 3, with two K steps of global loads in flight
+//   7: as 0, with two K steps of global loads in flight
 // ORCA_GEMM_VARIANT=<n> pins the variant (tests and tuning runs).
 static int choose_variant(int m, int n) {
   if (const char* f = getenv("ORCA_GEMM_VARIANT")) {
@@ -349,10 +343,11 @@ static int choose_variant(int m, int n) {
     if (v >= 0 && v <= 7) return v;
   }
   // measured on MI355X at the 13B / 175B layer shapes: the 8-wave 256 x 256
-  // tile (variant 3) is fastest once it yields enough tiles to spread over
-  // the 256 CUs; below that the 128 x 128 tile keeps more CUs busy
+  // tile with two K steps in flight (variant 6) is fastest once it yields
+  // enough tiles to spread over the 256 CUs; below that the 128 x 128 tile
+  // (variant 7) keeps more CUs busy
   const long big = (long)((m + 255) / 256) * ((n + 255) / 256);
-  return big >= 128 ? 3 : 0;
+  return big >= 128 ? 6 : 7;
 }
 
 template <int EPI, int WGM, int WGN, int TI, int TJ, bool PIPE = false>
@@ -375,9 +370,15 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
       case 3: launch_mfma<EPI, 4, 2, 2, 4>(a, w, bias, ep, m, n, k, s); break;
       case 4: launch_mfma<EPI, 2, 4, 2, 2>(a, w, bias, ep, m, n, k, s); break;
       case 5: launch_mfma<EPI, 4, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;
-      case 6: launch_mfma<EPI, 4, 2, 2, 4, true>(a, w, bias, ep, m, n, k, s); break;
-      case 7: launch_mfma<EPI, 2, 2, 2, 2, true>(a, w, bias, ep, m, n, k, s); break;
-      default: launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;
+      case 6:
+        if ((k / BK) % 2 == 0) launch_mfma<EPI, 4, 2, 2, 4, true>(a, w, bias, ep, m, n, k, s);
+        else launch_mfma<EPI, 4, 2, 2, 4>(a, w, bias, ep, m, n, k, s);
+        break;
+      case 7:
+        if ((k / BK) % 2 == 0) launch_mfma<EPI, 2, 2, 2, 2, true>(a, w, bias, ep, m, n, k, s);
+        else launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s);
+        break;
+      default: launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;  // 0
     }
   } else {
     hipLaunchKernelGGL(gemm_f32_kernel<EPI>, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, s,
