@@ -67,6 +67,31 @@ def time_events(fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
+def source_hash(files):
+    import hashlib
+    m = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "orca_selective_iteration_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    return m.hexdigest()[:16]
+
+
+def measured_traffic(workload, key, files):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs, scaled by the plain-copy calibration; None when no
+    counters exist for this workload or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(key)
+    if not rec or rec.get("source_hash") != source_hash(files):
+        return None
+    return {"bytes": int(rec["fetch_bytes"] + rec["write_bytes"]),
+            "read_bytes": int(rec["fetch_bytes"]), "write_bytes": int(rec["write_bytes"]),
+            "kernel": rec["kernel"]}
+
+
 def cpu_baseline(model, work, x_dev, layers_total):
     """The CPU oracle on layer 0 of the same batch (all rows, all requests),
     fp32 numpy on the host; tokens/s extrapolated to the model's depth."""
@@ -161,10 +186,13 @@ def main():
         gms = time_events(ffn1, args.kernel_reps, stream)
         tflops = 2.0 * M * F * H / (gms * 1e-3) / 1e12
         peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
-        gemm = {"bound": "mfma", "kernel": "gemm_bf16_kernel<gelu> (FFN1)" if bf16 else
-                "gemm_f32_kernel<gelu> (FFN1)", "shape": [M, F, H],
+        tr = measured_traffic(work.name, "gemm_ffn1", ["gemm.hip", "device.h", "kernels.h"])
+        gemm = {"bound": "mfma", "kernel": (tr["kernel"] if tr else "gemm_bf16_kernel<gelu>") +
+                " (FFN1)" if bf16 else "gemm_f32_kernel<gelu> (FFN1)", "shape": [M, F, H],
                 "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(tflops / peak, 4), "traffic": None, "ms_per_launch": round(gms, 4)}
+                "frac": round(tflops / peak, 4), "traffic": tr["bytes"] if tr else None,
+                "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
+                "algorithmic_flops": 2 * M * F * H, "ms_per_launch": round(gms, 4)}
         log(f"FFN1 GEMM {M}x{F}x{H}: {gms:.3f} ms, {tflops:.1f} TFLOP/s")
         del a, f
 
@@ -184,10 +212,11 @@ def main():
         esz = 2 if bf16 else 4
         nbytes = sum(2 * (work.kv_len[i] + 1) * H * esz for i in incr)
         gbs = nbytes / (dms * 1e-3) / 1e9
+        tr = measured_traffic(work.name, "decode", ["attn.hip", "device.h", "kernels.h"])
         decode = {"bound": "hbm", "kernel": "attn_split_kernel + attn_combine_kernel "
                   "(increment rows, one layer)", "achieved": round(gbs, 1),
                   "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                  "traffic": None, "ms_per_launch": round(dms, 4),
+                  "traffic": tr["bytes"] if tr else None, "ms_per_launch": round(dms, 4),
                   "algorithmic_bytes": nbytes}
         log(f"decode attention ({n} requests, one layer): {dms:.3f} ms, {gbs:.0f} GB/s")
 
