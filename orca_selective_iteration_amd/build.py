@@ -69,6 +69,14 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     objs = [s[-1] for s in steps]
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    # a kernel whose host-side launch stub failed to instantiate leaves an
+    # undefined symbol that only shows when the library is loaded
+    import ctypes
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        os.remove(tmp)
+        raise RuntimeError(f"built library does not load: {e}")
     os.replace(tmp, LIB)
     return LIB
 

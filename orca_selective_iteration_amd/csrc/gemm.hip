@@ -329,18 +329,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 // Tile shape for an M x N output.  Variants (wave grid x per-wave tiles):
 //   0: 2x2 waves, 2x2 tiles -> 128 x 128, 256 threads, 2 workgroups / CU
-//   1: 2x2 waves, 4x4 tiles -> 256 x 256, 256 threads
-//   2: 2x4 waves, 4x2 tiles -> 256 x 256, 512 threads
 //   3: 4x2 waves, 2x4 tiles -> 256 x 256, 512 threads
-//   4: 2x4 waves, 2x2 tiles -> 128 x 256, 512 threads
-//   5: 4x2 waves, 2x2 tiles -> 256 x 128, 512 threads
-//   6: as 3, with two K steps of global loads in flight
-//   7: as 0, with two K steps of global loads in flight
+//   6: as 3, with two K steps of global loads in flight (default, large)
+//   7: as 0, with two K steps of global loads in flight (default, small)
+// (6 and 7 need an even number of K steps and fall back to 3 and 0.)
 // ORCA_GEMM_VARIANT=<n> pins the variant (tests and tuning runs).
 static int choose_variant(int m, int n) {
   if (const char* f = getenv("ORCA_GEMM_VARIANT")) {
     const int v = atoi(f);
-    if (v >= 0 && v <= 7) return v;
+    if (v == 0 || v == 3 || v == 6 || v == 7) return v;
   }
   // measured on MI355X at the 13B / 175B layer shapes: the 8-wave 256 x 256
   // tile with two K steps in flight (variant 6) is fastest once it yields
@@ -365,11 +362,7 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
                          const EpiParams& ep, int m, int n, int k, hipStream_t s) {
   if (dtype == ORCA_BF16) {
     switch (choose_variant(m, n)) {
-      case 1: launch_mfma<EPI, 2, 2, 4, 4>(a, w, bias, ep, m, n, k, s); break;
-      case 2: launch_mfma<EPI, 2, 4, 4, 2>(a, w, bias, ep, m, n, k, s); break;
       case 3: launch_mfma<EPI, 4, 2, 2, 4>(a, w, bias, ep, m, n, k, s); break;
-      case 4: launch_mfma<EPI, 2, 4, 2, 2>(a, w, bias, ep, m, n, k, s); break;
-      case 5: launch_mfma<EPI, 4, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;
       case 6:
         if ((k / BK) % 2 == 0) launch_mfma<EPI, 4, 2, 2, 4, true>(a, w, bias, ep, m, n, k, s);
         else launch_mfma<EPI, 4, 2, 2, 4>(a, w, bias, ep, m, n, k, s);
