@@ -202,8 +202,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   uint16_t* sK = smem;
   uint16_t* sV = smem + BKV * KLD;
 
-  const PrefillItem it = a.pf[blockIdx.x];
-  const int h = blockIdx.y;
+  // grid (heads, items): all heads of the first (longest) item go first
+  const PrefillItem it = a.pf[blockIdx.y];
+  const int h = blockIdx.x;
   const DevReq rq = a.reqs[it.req];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -346,7 +347,7 @@ template <typename T, int D>
 static void launch_split(const AttnArgs& a, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     if (a.n_pf > 0)
-      hipLaunchKernelGGL((attn_prefill_kernel<D>), dim3(a.n_pf, a.heads), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_prefill_kernel<D>), dim3(a.heads, a.n_pf), dim3(256), 0, s, a);
   }
   if (a.n_items == 0) return;
   hipLaunchKernelGGL((attn_split_kernel<T, D>), dim3(a.n_items, a.heads), dim3(256), 0, s, a);

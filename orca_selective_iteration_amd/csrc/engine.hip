@@ -183,6 +183,11 @@ void build_plan(const orca_ctx* c, const orca_req_desc* reqs, int32_t n, int32_t
   p.n_items = ni;
   p.n_srows = ns;
   p.n_pf = np;
+  // causal prefill tiles cost ~ their last query position: dispatch the
+  // longest first so the short ones fill in behind them
+  std::sort(p.pf, p.pf + np, [](const PrefillItem& a, const PrefillItem& b) {
+    return a.q1 != b.q1 ? a.q1 > b.q1 : a.req < b.req;
+  });
 }
 
 orca_status hip_fail(hipError_t e, const char* what) {
