@@ -177,10 +177,12 @@ def main():
         a = synth.device_normal_(torch.empty((M, H), dtype=model.tdt, device="cuda"), 11)
         f = torch.empty((M, F), dtype=model.tdt, device="cuda")
         w = model.weights[0]
+        gws_bytes = L.orca_op_linear_workspace_bytes(model.odt, M, F, H)
+        gws = torch.empty(max(gws_bytes, 1), dtype=torch.uint8, device="cuda")
 
         def ffn1():
             L.orca_op_linear(model.odt, L.ORCA_EPI_BIAS_GELU, a, w["w_1"], w["b_1"], f, M, F, H,
-                             stream)
+                             gws, gws_bytes, stream=stream)
         for _ in range(3):
             ffn1()
         gms = time_events(ffn1, args.kernel_reps, stream)

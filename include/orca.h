@@ -212,22 +212,31 @@ typedef enum {
 
 /* acc[m][n] = sum_k a[m][k] * w[n][k] on a device [m][k], w device [n][k],
  * bias device [n] (all `dtype`), then the epilogue.  m >= 0; n % 64 == 0 and
- * k % 64 == 0.  bf16 runs on the MFMA units. */
+ * k % 64 == 0.  bf16 runs on the MFMA units.
+ * workspace: device scratch owned by the caller, may be NULL.  For bf16 and
+ * m <= 64 rows (batches made mostly of increment rows: the weights are
+ * streamed once and the arithmetic is light) a split-K path runs when
+ * ws_bytes >= orca_op_linear_workspace_bytes(dtype, m, n, k); it writes fp32
+ * partial sums there.  Otherwise the tiled path runs and the workspace is
+ * not touched.  Both paths accumulate in fp32; only the summation order
+ * differs. */
+size_t orca_op_linear_workspace_bytes(int32_t dtype, int32_t m, int32_t n, int32_t k);
 orca_status orca_op_linear(int32_t dtype, int32_t epilogue, const void* a, const void* w,
                            const void* bias, void* out, int32_t m, int32_t n, int32_t k,
-                           void* stream);
+                           void* workspace, size_t ws_bytes, void* stream);
 
 /* The fused QKV projection with the K/V manager's append: for every row m,
  * [q|k|v] = a[m] W_qkv^T + b_qkv; q goes to q_out[m][0..H-1]; k and v of
  * head h go to k_pool_l[h][row_dst[m]][..] and v_pool_l[h][row_dst[m]][..].
  * row_dst: device int32 [m], each in [0, kv_capacity).  k_pool_l/v_pool_l
- * point at one layer's pool [heads][kv_capacity][d].  ([houmin] 3.1.2: the
+ * point at one layer's pool [heads][kv_capacity][d].  workspace / ws_bytes
+ * as for orca_op_linear with n = 3 * hidden, k = hidden.  ([houmin] 3.1.2: the
  * QKV Linear yields 3H columns; the split before attention is index
  * arithmetic; the new K/V of every token is appended to its request.) */
 orca_status orca_op_qkv(int32_t dtype, const void* a, const void* w_qkv, const void* b_qkv,
                         void* q_out, void* k_pool_l, void* v_pool_l, const int32_t* row_dst,
                         int32_t m, int32_t hidden, int32_t heads, int64_t kv_capacity,
-                        void* stream);
+                        void* workspace, size_t ws_bytes, void* stream);
 
 /* Split attention of one layer ([houmin] 3.1.2): every request attends
  * separately over its own K/V (initiation: causal over its prompt;

@@ -52,6 +52,7 @@ struct orca_ctx {
   // workspace layout
   size_t off_resid = 0, off_a = 0, off_q = 0, off_o = 0, off_f = 0;
   size_t off_part_o = 0, off_part_ml = 0, off_meta = 0, ws_bytes = 0, meta_bytes = 0;
+  size_t off_gpart = 0, gpart_bytes = 0;   // split-K partial sums of the few-rows Linear path
   // pinned staging ring for the metadata
   void* staging[NSLOT] = {};
   hipEvent_t ev[NSLOT] = {};
@@ -298,6 +299,15 @@ orca_status orca_create(const orca_model_desc* desc, const orca_layer_weights* l
   c->off_f = take(R * F * s);
   c->off_part_o = take(size_t(c->max_items) * H * 4);
   c->off_part_ml = take(size_t(c->max_items) * d.heads * 2 * 4);
+  {
+    const int m = std::min<int>(max_rows, SKINNY_MAX_M);
+    const int hh = d.hidden, ff = d.ffn;
+    c->gpart_bytes = std::max({linear_workspace_bytes(d.dtype, m, 3 * hh, hh),
+                               linear_workspace_bytes(d.dtype, m, hh, hh),
+                               linear_workspace_bytes(d.dtype, m, ff, hh),
+                               linear_workspace_bytes(d.dtype, m, hh, ff)});
+  }
+  c->off_gpart = take(c->gpart_bytes);
   c->meta_bytes = sizeof(DevReq) * max_reqs + sizeof(int32_t) * R +
                   sizeof(SplitItem) * c->max_items + sizeof(SplitRow) * R +
                   sizeof(PrefillItem) * c->max_pf + 16 * 8;
@@ -373,6 +383,8 @@ orca_status orca_iteration(orca_ctx* c, const orca_req_desc* reqs, int32_t n_req
   void* f = ws + c->off_f;
   const int32_t* row_dst = reinterpret_cast<const int32_t*>(ws + c->off_meta + p.off_row_dst);
   const size_t pool = c->layer_pool_elems() * dsize(dt);
+  void* gp = ws + c->off_gpart;
+  const size_t gpb = c->gpart_bytes;
 
   HIP_TRY(launch_to_f32(dt, x, resid, int64_t(R) * H, s), "input conversion");
   for (int l = 0; l < d.layers; ++l) {
@@ -380,14 +392,14 @@ orca_status orca_iteration(orca_ctx* c, const orca_req_desc* reqs, int32_t n_req
     QkvDest qd{q, static_cast<char*>(c->k_pool) + pool * l, static_cast<char*>(c->v_pool) + pool * l,
                row_dst, H, H / d.heads, d.kv_capacity};
     HIP_TRY(launch_layernorm(dt, resid, w.ln1_g, w.ln1_b, a, R, H, d.ln_eps, s), "LN1");
-    HIP_TRY(launch_linear(dt, EPI_QKV, a, w.w_qkv, w.b_qkv, nullptr, &qd, R, 3 * H, H, s), "QKV");
+    HIP_TRY(launch_linear(dt, EPI_QKV, a, w.w_qkv, w.b_qkv, nullptr, &qd, R, 3 * H, H, gp, gpb, s), "QKV");
     st = run_attention(c, l, aa, q, o, s);
     if (st != ORCA_OK) return st;
-    HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_RESID, o, w.w_o, w.b_o, resid, nullptr, R, H, H, s),
+    HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_RESID, o, w.w_o, w.b_o, resid, nullptr, R, H, H, gp, gpb, s),
             "output projection");
     HIP_TRY(launch_layernorm(dt, resid, w.ln2_g, w.ln2_b, a, R, H, d.ln_eps, s), "LN2");
-    HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_GELU, a, w.w_1, w.b_1, f, nullptr, R, F, H, s), "FFN1");
-    HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_RESID, f, w.w_2, w.b_2, resid, nullptr, R, H, F, s),
+    HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_GELU, a, w.w_1, w.b_1, f, nullptr, R, F, H, gp, gpb, s), "FFN1");
+    HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_RESID, f, w.w_2, w.b_2, resid, nullptr, R, H, F, gp, gpb, s),
             "FFN2");
   }
   HIP_TRY(launch_from_f32(dt, resid, y, int64_t(R) * H, s), "output conversion");
@@ -409,9 +421,14 @@ orca_status orca_op_layernorm(int32_t dtype, const float* x, const void* gamma, 
   return ORCA_OK;
 }
 
+size_t orca_op_linear_workspace_bytes(int32_t dtype, int32_t m, int32_t n, int32_t k) {
+  if (m < 0 || n < 64 || k < 64 || n % 64 || k % 64) return 0;
+  return linear_workspace_bytes(dtype, m, n, k);
+}
+
 orca_status orca_op_linear(int32_t dtype, int32_t epilogue, const void* a, const void* w,
                            const void* bias, void* out, int32_t m, int32_t n, int32_t k,
-                           void* stream) {
+                           void* workspace, size_t ws_bytes, void* stream) {
   clear_error();
   ORCA_CHECK_ARG(dtype == ORCA_F32 || dtype == ORCA_BF16, "unknown dtype %d", dtype);
   ORCA_CHECK_ARG(epilogue >= ORCA_EPI_BIAS && epilogue <= ORCA_EPI_BIAS_RESID,
@@ -422,7 +439,7 @@ orca_status orca_op_linear(int32_t dtype, int32_t epilogue, const void* a, const
     return ORCA_ERR_UNSUPPORTED;
   }
   ORCA_CHECK_ARG(m == 0 || (a && w && bias && out), "NULL argument");
-  HIP_TRY(launch_linear(dtype, epilogue, a, w, bias, out, nullptr, m, n, k,
+  HIP_TRY(launch_linear(dtype, epilogue, a, w, bias, out, nullptr, m, n, k, workspace, ws_bytes,
                         static_cast<hipStream_t>(stream)), "linear launch");
   return ORCA_OK;
 }
@@ -430,7 +447,7 @@ orca_status orca_op_linear(int32_t dtype, int32_t epilogue, const void* a, const
 orca_status orca_op_qkv(int32_t dtype, const void* a, const void* w_qkv, const void* b_qkv,
                         void* q_out, void* k_pool_l, void* v_pool_l, const int32_t* row_dst,
                         int32_t m, int32_t hidden, int32_t heads, int64_t kv_capacity,
-                        void* stream) {
+                        void* workspace, size_t ws_bytes, void* stream) {
   clear_error();
   ORCA_CHECK_ARG(dtype == ORCA_F32 || dtype == ORCA_BF16, "unknown dtype %d", dtype);
   ORCA_CHECK_ARG(m >= 0 && hidden >= 64 && heads >= 1 && hidden % heads == 0 && kv_capacity >= 1,
@@ -444,6 +461,7 @@ orca_status orca_op_qkv(int32_t dtype, const void* a, const void* w_qkv, const v
                  "NULL argument");
   QkvDest qd{q_out, k_pool_l, v_pool_l, row_dst, hidden, hidden / heads, kv_capacity};
   HIP_TRY(launch_linear(dtype, EPI_QKV, a, w_qkv, b_qkv, nullptr, &qd, m, 3 * hidden, hidden,
+                        workspace, ws_bytes,
                         static_cast<hipStream_t>(stream)), "qkv launch");
   return ORCA_OK;
 }

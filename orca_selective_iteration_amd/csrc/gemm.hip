@@ -26,6 +26,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "device.h"
@@ -83,7 +84,7 @@ struct EpiCol {
   // `row` is m, `dst` its pool slot (QKV only)
   __device__ __forceinline__ void store(int row, int dst, float v) const {
     T* p = ptr + (size_t)(slot ? dst : row) * stride;
-    if constexpr (EPI == ORCA_EPI_BIAS || EPI == EPI_QKV) {
+    if constexpr (EPI == ORCA_EPI_BIAS || EPI == EPI_QKV || EPI == EPI_PARTIAL) {
       store_f32(p, v);
     } else if constexpr (EPI == ORCA_EPI_BIAS_GELU) {
       store_f32(p, gelu_tanh(v));
@@ -116,8 +117,15 @@ template <int EPI, int WGM, int WGN, int TI, int TJ, bool PIPE>
 __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && TI * TJ <= 4) ? 2 : 1)
 void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
                       const bf16* __restrict__ bias, EpiParams ep, int M, int N, int K,
-                      int tiles_m) {
+                      int tiles_m, int kt_per_split) {
   using C = TileCfg<WGM, WGN, TI, TJ>;
+  // grid.y splits K: this workgroup sums K steps [k0, k0 + KT) (the whole
+  // of K unless the epilogue writes fp32 partial sums)
+  const int k0 = blockIdx.y * kt_per_split;
+  const int KT = min(K / BK - k0, kt_per_split);
+  A += (size_t)k0 * BK;
+  W += (size_t)k0 * BK;
+  if constexpr (EPI == EPI_PARTIAL) ep.out = static_cast<float*>(ep.out) + (size_t)blockIdx.y * M * N;
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][C::BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][C::BN * LDK];
 
@@ -161,7 +169,6 @@ void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
   for (int i = 0; i < C::LB; ++i) *reinterpret_cast<uint4*>(&sB[0][oB[i]]) = rb[i];
   __syncthreads();
 
-  const int KT = K / BK;
   const int fr = lane & 31, fk = (lane >> 5) * 8;
   const int a_off = (wm * 32 * TI + fr) * LDK + fk, b_off = (wn * 32 * TJ + fr) * LDK + fk;
   if constexpr (!PIPE) {
@@ -256,11 +263,13 @@ void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
 
   // 32x32 accumulator layout: lane holds column lane%32 and rows
   // 8*(r/4) + 4*(lane/32) + r%4 for its 16 registers r.
-  using OutT = typename std::conditional<EPI == ORCA_EPI_BIAS_RESID, float, bf16>::type;
+  using OutT = typename std::conditional<EPI == ORCA_EPI_BIAS_RESID || EPI == EPI_PARTIAL, float,
+                                         bf16>::type;
   float bn[TJ];
 #pragma unroll
   for (int j = 0; j < TJ; ++j)
-    bn[j] = load_f32(bias + min(tn * C::BN + wn * 32 * TJ + j * 32 + fr, N - 1));
+    bn[j] = EPI == EPI_PARTIAL ? 0.f
+                               : load_f32(bias + min(tn * C::BN + wn * 32 * TJ + j * 32 + fr, N - 1));
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
     const int n = tn * C::BN + wn * 32 * TJ + j * 32 + fr;
@@ -274,6 +283,42 @@ void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
         if (m < M) col.store(m, EPI == EPI_QKV ? ep.qkv.row_dst[m] : 0, acc[i][j][r] + bn[j]);
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------- few rows
+
+// Few rows (M <= 64: iterations made mostly of increment rows) make the
+// Linear layers weight-streaming: every weight is read once per iteration
+// and the MFMA units idle, while 256 x 256 or 128 x 128 tiles would leave
+// most CUs without work (a 5120-column layer has 40 of them).  That path
+// runs the kernel above on 32 x 128 or 64 x 128 tiles with grid.y
+// splitting K (EPI_PARTIAL: fp32 partial sums to [splits][M][N], no bias),
+// so the grid holds enough workgroups to keep HBM busy with the same
+// coalesced 128-byte row loads; this kernel then adds the splits, the bias
+// and the epilogue, four columns per thread.
+template <int EPI>
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ part,
+                                                            int splits,
+                                                            const bf16* __restrict__ bias,
+                                                            EpiParams ep, int M, int N) {
+  using OutT = typename std::conditional<EPI == ORCA_EPI_BIAS_RESID, float, bf16>::type;
+  const int n4 = N / 4;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * n4) return;
+  const int m = idx / n4, n = (idx - m * n4) * 4;
+  const size_t stride = (size_t)M * N;
+  float4 v = *reinterpret_cast<const float4*>(part + (size_t)m * N + n);
+  for (int s = 1; s < splits; ++s) {
+    const float4 t = *reinterpret_cast<const float4*>(part + s * stride + (size_t)m * N + n);
+    v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+  }
+  const int dst = EPI == EPI_QKV ? ep.qkv.row_dst[m] : 0;
+  const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const EpiCol<OutT, EPI> col(ep, n + c);
+    col.store(m, dst, vv[c] + load_f32(bias + n + c));
   }
 }
 
@@ -332,13 +377,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 //   3: 4x2 waves, 2x4 tiles -> 256 x 256, 512 threads
 //   6: as 3, with two K steps of global loads in flight (default, large)
 //   7: as 0, with two K steps of global loads in flight (default, small)
+//  10: the few-rows split-K path (default for M <= SKINNY_MAX_M when the
+//      caller passes a large enough workspace; else variant 7)
 // (6 and 7 need an even number of K steps and fall back to 3 and 0.)
 // ORCA_GEMM_VARIANT=<n> pins the variant (tests and tuning runs).
 static int choose_variant(int m, int n) {
   if (const char* f = getenv("ORCA_GEMM_VARIANT")) {
     const int v = atoi(f);
-    if (v == 0 || v == 3 || v == 6 || v == 7) return v;
+    if (v == 0 || v == 3 || v == 6 || v == 7 || v == 10) return v;
   }
+  if (m <= SKINNY_MAX_M) return -1;
   // measured on MI355X at the 13B / 175B layer shapes: the 8-wave 256 x 256
   // tile with two K steps in flight (variant 6) is fastest once it yields
   // enough tiles to spread over the 256 CUs; below that the 128 x 128 tile
@@ -349,29 +397,88 @@ static int choose_variant(int m, int n) {
 
 template <int EPI, int WGM, int WGN, int TI, int TJ, bool PIPE = false>
 static void launch_mfma(const void* a, const void* w, const void* bias, const EpiParams& ep, int m,
-                        int n, int k, hipStream_t s) {
+                        int n, int k, hipStream_t s, int splits = 1, int kt_per_split = 0) {
   using C = TileCfg<WGM, WGN, TI, TJ>;
   const int tiles_m = (m + C::BM - 1) / C::BM, tiles_n = (n + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WGM, WGN, TI, TJ, PIPE>), dim3(tiles_m * tiles_n),
-                     dim3(C::NT), 0, s, (const bf16*)a, (const bf16*)w, (const bf16*)bias, ep, m,
-                     n, k, tiles_m);
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WGM, WGN, TI, TJ, PIPE>),
+                     dim3(tiles_m * tiles_n, splits), dim3(C::NT), 0, s, (const bf16*)a,
+                     (const bf16*)w, (const bf16*)bias, ep, m, n, k, tiles_m,
+                     kt_per_split > 0 ? kt_per_split : k / BK);
+}
+
+// Split-K plan of the few-rows path for an m x n x k problem (bf16,
+// m <= SKINNY_MAX_M, k % 64 == 0, n % 4 == 0): one 32*mt x 128 tile per
+// workgroup (four waves side by side along N), grid.y splits the K steps
+// into an even count per split, sized so the grid holds about
+// SKINNY_TARGET_WG workgroups.
+struct SkinnyPlan {
+  int mt, tiles, kt_per_split, splits;
+};
+constexpr int SKINNY_TARGET_WG = 512;
+static bool skinny_plan(int m, int n, int k, SkinnyPlan& p) {
+  if (m < 1 || m > SKINNY_MAX_M || k % BK || n % 4) return false;
+  p.mt = m <= 32 ? 1 : 2;
+  p.tiles = (n + 127) / 128;
+  const int kt = k / BK;
+  int target = SKINNY_TARGET_WG;
+  if (const char* f = getenv("ORCA_SKINNY_TARGET")) target = std::max(1, atoi(f));
+  int splits = std::max(1, std::min({(target + p.tiles - 1) / p.tiles, SKINNY_MAX_SPLITS,
+                                     std::max(1, kt / 4)}));
+  int per = (kt + splits - 1) / splits;
+  if (kt % 2 == 0) per += per & 1;   // even K steps per split: the two-step pipeline
+  p.kt_per_split = per;
+  p.splits = (kt + per - 1) / per;
+  return true;
+}
+
+size_t linear_workspace_bytes(int dtype, int m, int n, int k) {
+  SkinnyPlan p;
+  if (dtype != ORCA_BF16 || !skinny_plan(m, n, k, p)) return 0;
+  return (size_t)p.splits * m * n * sizeof(float);
+}
+
+template <int EPI>
+static void launch_skinny(const SkinnyPlan& p, const void* a, const void* w, const void* bias,
+                          const EpiParams& ep, float* part, int m, int n, int k, hipStream_t s) {
+  EpiParams pp{};
+  pp.out = part;
+  pp.ldo = n;
+  const bool pipe = p.kt_per_split % 2 == 0 && (k / BK) % 2 == 0;
+  if (p.mt == 1) {
+    if (pipe) launch_mfma<EPI_PARTIAL, 1, 4, 1, 1, true>(a, w, bias, pp, m, n, k, s, p.splits, p.kt_per_split);
+    else launch_mfma<EPI_PARTIAL, 1, 4, 1, 1>(a, w, bias, pp, m, n, k, s, p.splits, p.kt_per_split);
+  } else {
+    if (pipe) launch_mfma<EPI_PARTIAL, 1, 4, 2, 1, true>(a, w, bias, pp, m, n, k, s, p.splits, p.kt_per_split);
+    else launch_mfma<EPI_PARTIAL, 1, 4, 2, 1>(a, w, bias, pp, m, n, k, s, p.splits, p.kt_per_split);
+  }
+  const int threads = m * (n / 4);
+  hipLaunchKernelGGL(skinny_reduce_kernel<EPI>, dim3((threads + 255) / 256), dim3(256), 0, s,
+                     part, p.splits, (const bf16*)bias, ep, m, n);
 }
 
 template <int EPI>
 static void launch_typed(int dtype, const void* a, const void* w, const void* bias,
-                         const EpiParams& ep, int m, int n, int k, hipStream_t s) {
+                         const EpiParams& ep, void* ws, size_t ws_bytes, int m, int n, int k,
+                         hipStream_t s) {
   if (dtype == ORCA_BF16) {
-    switch (choose_variant(m, n)) {
+    SkinnyPlan sp;
+    const int v = choose_variant(m, n);
+    if ((v == 10 || v < 0) && ws && skinny_plan(m, n, k, sp) &&
+        ws_bytes >= (size_t)sp.splits * m * n * sizeof(float)) {
+      launch_skinny<EPI>(sp, a, w, bias, ep, static_cast<float*>(ws), m, n, k, s);
+      return;
+    }
+    switch (v) {
+      case 0: launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;
       case 3: launch_mfma<EPI, 4, 2, 2, 4>(a, w, bias, ep, m, n, k, s); break;
       case 6:
         if ((k / BK) % 2 == 0) launch_mfma<EPI, 4, 2, 2, 4, true>(a, w, bias, ep, m, n, k, s);
         else launch_mfma<EPI, 4, 2, 2, 4>(a, w, bias, ep, m, n, k, s);
         break;
-      case 7:
+      default:  // 7, and the few-rows choice when no workspace was given
         if ((k / BK) % 2 == 0) launch_mfma<EPI, 2, 2, 2, 2, true>(a, w, bias, ep, m, n, k, s);
         else launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s);
         break;
-      default: launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;  // 0
     }
   } else {
     hipLaunchKernelGGL(gemm_f32_kernel<EPI>, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, s,
@@ -380,17 +487,24 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
 }
 
 hipError_t launch_linear(int dtype, int epilogue, const void* a, const void* w, const void* bias,
-                         void* out, const QkvDest* qkv, int m, int n, int k, hipStream_t s) {
+                         void* out, const QkvDest* qkv, int m, int n, int k, void* ws,
+                         size_t ws_bytes, hipStream_t s) {
   if (m == 0) return hipSuccess;
   EpiParams ep{};
   ep.out = out;
   ep.ldo = n;
   if (qkv) ep.qkv = *qkv;
   switch (epilogue) {
-    case ORCA_EPI_BIAS: launch_typed<ORCA_EPI_BIAS>(dtype, a, w, bias, ep, m, n, k, s); break;
-    case ORCA_EPI_BIAS_GELU: launch_typed<ORCA_EPI_BIAS_GELU>(dtype, a, w, bias, ep, m, n, k, s); break;
-    case ORCA_EPI_BIAS_RESID: launch_typed<ORCA_EPI_BIAS_RESID>(dtype, a, w, bias, ep, m, n, k, s); break;
-    default: launch_typed<EPI_QKV>(dtype, a, w, bias, ep, m, n, k, s); break;
+    case ORCA_EPI_BIAS:
+      launch_typed<ORCA_EPI_BIAS>(dtype, a, w, bias, ep, ws, ws_bytes, m, n, k, s);
+      break;
+    case ORCA_EPI_BIAS_GELU:
+      launch_typed<ORCA_EPI_BIAS_GELU>(dtype, a, w, bias, ep, ws, ws_bytes, m, n, k, s);
+      break;
+    case ORCA_EPI_BIAS_RESID:
+      launch_typed<ORCA_EPI_BIAS_RESID>(dtype, a, w, bias, ep, ws, ws_bytes, m, n, k, s);
+      break;
+    default: launch_typed<EPI_QKV>(dtype, a, w, bias, ep, ws, ws_bytes, m, n, k, s); break;
   }
   return hipGetLastError();
 }

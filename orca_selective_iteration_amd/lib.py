@@ -76,8 +76,9 @@ def _declare(lib):
         "orca_workspace_bytes": (S, [V]),
         "orca_iteration": (c_int32, [V, POINTER(orca_req_desc), I32, V, V, V, S, V]),
         "orca_op_layernorm": (c_int32, [I32, V, V, V, V, I32, I32, c_float, V]),
-        "orca_op_linear": (c_int32, [I32, I32, V, V, V, V, I32, I32, I32, V]),
-        "orca_op_qkv": (c_int32, [I32, V, V, V, V, V, V, V, I32, I32, I32, I64, V]),
+        "orca_op_linear_workspace_bytes": (S, [I32, I32, I32, I32]),
+        "orca_op_linear": (c_int32, [I32, I32, V, V, V, V, I32, I32, I32, V, S, V]),
+        "orca_op_qkv": (c_int32, [I32, V, V, V, V, V, V, V, I32, I32, I32, I64, V, S, V]),
         "orca_op_attention": (c_int32, [V, I32, POINTER(orca_req_desc), I32, V, V, V, S, V]),
         "orca_sched_create": (c_int32, [V, I32, I32, I32, POINTER(V)]),
         "orca_sched_destroy": (None, [V]),
@@ -227,17 +228,23 @@ def orca_op_layernorm(dtype: int, x, gamma, beta, out, rows: int, hidden: int, e
                                     hidden, eps, stream_handle(stream)), "orca_op_layernorm")
 
 
+def orca_op_linear_workspace_bytes(dtype: int, m: int, n: int, k: int) -> int:
+    return int(load().orca_op_linear_workspace_bytes(dtype, m, n, k))
+
+
 def orca_op_linear(dtype: int, epilogue: int, a, w, bias, out, m: int, n: int, k: int,
-                   stream=None) -> None:
+                   workspace=None, ws_bytes: int = 0, stream=None) -> None:
     _check(load().orca_op_linear(dtype, epilogue, ptr(a), ptr(w), ptr(bias), ptr(out), m, n, k,
-                                 stream_handle(stream)), "orca_op_linear")
+                                 ptr(workspace), ws_bytes, stream_handle(stream)),
+           "orca_op_linear")
 
 
 def orca_op_qkv(dtype: int, a, w_qkv, b_qkv, q_out, k_pool_l, v_pool_l, row_dst, m: int,
-                hidden: int, heads: int, kv_capacity: int, stream=None) -> None:
+                hidden: int, heads: int, kv_capacity: int, workspace=None, ws_bytes: int = 0,
+                stream=None) -> None:
     _check(load().orca_op_qkv(dtype, ptr(a), ptr(w_qkv), ptr(b_qkv), ptr(q_out), ptr(k_pool_l),
                               ptr(v_pool_l), ptr(row_dst), m, hidden, heads, kv_capacity,
-                              stream_handle(stream)), "orca_op_qkv")
+                              ptr(workspace), ws_bytes, stream_handle(stream)), "orca_op_qkv")
 
 
 def orca_op_attention(ctx: int, layer: int, reqs: Sequence, q, o, workspace, ws_bytes: int,

@@ -64,13 +64,13 @@ LINEAR_CASES = [
     ("bf16", 1, 128, 64), ("bf16", 7, 192, 64), ("bf16", 130, 384, 256),
     ("bf16", 300, 1024, 1024), ("bf16", 257, 3072, 1024), ("bf16", 129, 128, 4096),
     ("f32", 7, 192, 64), ("f32", 65, 256, 128), ("f32", 1, 64, 64),
+    # few rows: the split-K weight-streaming path when a workspace is given
+    ("bf16", 33, 640, 2048), ("bf16", 64, 1536, 512), ("bf16", 31, 320, 4096),
+    ("bf16", 64, 128, 64),
 ]
 
 
-@pytest.mark.parametrize("epi", [L.ORCA_EPI_BIAS, L.ORCA_EPI_BIAS_GELU, L.ORCA_EPI_BIAS_RESID])
-@pytest.mark.parametrize("dtype,m,n,k", LINEAR_CASES)
-def test_linear(dtype, m, n, k, epi):
-    print(f"case linear {dtype} m={m} n={n} k={k} epi={epi}", flush=True)
+def _linear_case(dtype, m, n, k, epi, workspace):
     rng = np.random.default_rng(m * 1000 + n + k + epi)
     a = draw(rng, (m, k), 1.0, dtype)
     w = draw(rng, (n, k), 0.02 * 32 / np.sqrt(k), dtype)
@@ -84,8 +84,27 @@ def test_linear(dtype, m, n, k, epi):
         out = torch.empty((m, n), dtype=tdt(dtype), device=DEV)
         if epi == L.ORCA_EPI_BIAS_GELU:
             ref = om.gelu_tanh(ref)
-    L.orca_op_linear(odt(dtype), epi, dev(a, dtype), dev(w, dtype), dev(b, dtype), out, m, n, k)
-    assert rel_err(host(out), ref) < TOL[dtype]
+    ws, nb = None, 0
+    if workspace:
+        nb = L.orca_op_linear_workspace_bytes(odt(dtype), m, n, k)
+        # poison the partial buffer: every element it holds must be written
+        ws = torch.full((max(nb, 4) // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    L.orca_op_linear(odt(dtype), epi, dev(a, dtype), dev(w, dtype), dev(b, dtype), out, m, n, k,
+                     ws, nb)
+    return host(out), ref, nb
+
+
+@pytest.mark.parametrize("epi", [L.ORCA_EPI_BIAS, L.ORCA_EPI_BIAS_GELU, L.ORCA_EPI_BIAS_RESID])
+@pytest.mark.parametrize("dtype,m,n,k", LINEAR_CASES)
+@pytest.mark.parametrize("workspace", [False, True])
+def test_linear(dtype, m, n, k, epi, workspace):
+    print(f"case linear {dtype} m={m} n={n} k={k} epi={epi} ws={workspace}", flush=True)
+    got, ref, nb = _linear_case(dtype, m, n, k, epi, workspace)
+    if workspace:
+        # bf16 with at most 64 rows is exactly the set that takes the split-K path
+        assert (nb > 0) == (dtype == "bf16" and m <= 64)
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) < TOL[dtype]
 
 
 def test_linear_empty_batch_is_noop():
@@ -112,8 +131,10 @@ def test_qkv_split_and_append(dtype, m, hidden, heads):
     kp = torch.full((heads, cap, d), 7.0, dtype=tdt(dtype), device=DEV)
     vp = torch.full((heads, cap, d), -7.0, dtype=tdt(dtype), device=DEV)
     q = torch.empty((m, hidden), dtype=tdt(dtype), device=DEV)
+    nb = L.orca_op_linear_workspace_bytes(odt(dtype), m, 3 * hidden, hidden)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=DEV)
     L.orca_op_qkv(odt(dtype), dev(a, dtype), dev(w, dtype), dev(b, dtype), q, kp, vp,
-                  torch.from_numpy(dst).to(DEV), m, hidden, heads, cap)
+                  torch.from_numpy(dst).to(DEV), m, hidden, heads, cap, ws, nb)
     ref = om.linear(a.astype(np.float64), w.astype(np.float64), b.astype(np.float64))
     assert rel_err(host(q), ref[:, :hidden]) < TOL[dtype]
     kh, vh = host(kp), host(vp)
