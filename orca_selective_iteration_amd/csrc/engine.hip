@@ -299,10 +299,11 @@ orca_status orca_create(const orca_model_desc* desc, const orca_layer_weights* l
   c->off_f = take(R * F * s);
   c->off_part_o = take(size_t(c->max_items) * H * 4);
   c->off_part_ml = take(size_t(c->max_items) * d.heads * 2 * 4);
-  {
-    const int m = std::min<int>(max_rows, SKINNY_MAX_M);
+  // split-K partial sums of the Linear layers: the largest need over every
+  // row count the context accepts
+  for (int m = 1; m <= std::min<int>(max_rows, SPLIT_MAX_M); ++m) {
     const int hh = d.hidden, ff = d.ffn;
-    c->gpart_bytes = std::max({linear_workspace_bytes(d.dtype, m, 3 * hh, hh),
+    c->gpart_bytes = std::max({c->gpart_bytes, linear_workspace_bytes(d.dtype, m, 3 * hh, hh),
                                linear_workspace_bytes(d.dtype, m, hh, hh),
                                linear_workspace_bytes(d.dtype, m, ff, hh),
                                linear_workspace_bytes(d.dtype, m, hh, ff)});

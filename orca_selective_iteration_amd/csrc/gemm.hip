@@ -288,15 +288,15 @@ void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
 
 // ---------------------------------------------------------------- few rows
 
-// Few rows (M <= 64: iterations made mostly of increment rows) make the
-// Linear layers weight-streaming: every weight is read once per iteration
-// and the MFMA units idle, while 256 x 256 or 128 x 128 tiles would leave
-// most CUs without work (a 5120-column layer has 40 of them).  That path
-// runs the kernel above on 32 x 128 or 64 x 128 tiles with grid.y
-// splitting K (EPI_PARTIAL: fp32 partial sums to [splits][M][N], no bias),
-// so the grid holds enough workgroups to keep HBM busy with the same
-// coalesced 128-byte row loads; this kernel then adds the splits, the bias
-// and the epilogue, four columns per thread.
+// Few rows (iterations made mostly of increment rows) make the Linear
+// layers weight-streaming: every weight is read once per iteration and the
+// MFMA units idle, while 256 x 256 or 128 x 128 tiles would leave most CUs
+// without work (a 5120-column layer at 64 rows has 40 of them).  The
+// split-K path runs the kernel above on 32 x 128, 64 x 128 or 128 x 128
+// tiles with grid.y splitting K (EPI_PARTIAL: fp32 partial sums to
+// [splits][M][N], no bias), so the grid holds enough workgroups to keep HBM
+// busy with the same coalesced 128-byte row loads; this kernel then adds
+// the splits, the bias and the epilogue, four columns per thread.
 template <int EPI>
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ part,
                                                             int splits,
@@ -377,8 +377,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 //   3: 4x2 waves, 2x4 tiles -> 256 x 256, 512 threads
 //   6: as 3, with two K steps of global loads in flight (default, large)
 //   7: as 0, with two K steps of global loads in flight (default, small)
-//  10: the few-rows split-K path (default for M <= SKINNY_MAX_M when the
-//      caller passes a large enough workspace; else variant 7)
+//  10: split-K (default when the tiles are too few to fill the GPU, the
+//      rows are at most SPLIT_MAX_M and the caller passes a large enough
+//      workspace; else variant 7)
 // (6 and 7 need an even number of K steps and fall back to 3 and 0.)
 // ORCA_GEMM_VARIANT=<n> pins the variant (tests and tuning runs).
 static int choose_variant(int m, int n) {
@@ -386,13 +387,12 @@ static int choose_variant(int m, int n) {
     const int v = atoi(f);
     if (v == 0 || v == 3 || v == 6 || v == 7 || v == 10) return v;
   }
-  if (m <= SKINNY_MAX_M) return -1;
   // measured on MI355X at the 13B / 175B layer shapes: the 8-wave 256 x 256
   // tile with two K steps in flight (variant 6) is fastest once it yields
   // enough tiles to spread over the 256 CUs; below that the 128 x 128 tile
   // (variant 7) keeps more CUs busy
   const long big = (long)((m + 255) / 256) * ((n + 255) / 256);
-  return big >= 128 ? 6 : 7;
+  return big >= 128 ? 6 : -1;
 }
 
 template <int EPI, int WGM, int WGN, int TI, int TJ, bool PIPE = false>
@@ -406,51 +406,64 @@ static void launch_mfma(const void* a, const void* w, const void* bias, const Ep
                      kt_per_split > 0 ? kt_per_split : k / BK);
 }
 
-// Split-K plan of the few-rows path for an m x n x k problem (bf16,
-// m <= SKINNY_MAX_M, k % 64 == 0, n % 4 == 0): one 32*mt x 128 tile per
-// workgroup (four waves side by side along N), grid.y splits the K steps
-// into an even count per split, sized so the grid holds about
-// SKINNY_TARGET_WG workgroups.
-struct SkinnyPlan {
-  int mt, tiles, kt_per_split, splits;
+// Split-K plan for an m x n x k bf16 problem whose tiles are too few to
+// fill the GPU (k % 64 == 0, n % 4 == 0).  Tile by rows: 32 x 128 or
+// 64 x 128 (four waves side by side along N) up to 64 rows, else 128 x 128.
+// grid.y splits the K steps, an even count per split (the two-step
+// pipeline), so the grid holds about SPLIT_TARGET_WG workgroups; the fp32
+// partial buffer is then bounded by about SPLIT_TARGET_WG tile areas.
+struct SplitPlan {
+  int tile;   // 0: 32 x 128, 1: 64 x 128, 2: 128 x 128
+  int tiles, kt_per_split, splits;
 };
-constexpr int SKINNY_TARGET_WG = 512;
-static bool skinny_plan(int m, int n, int k, SkinnyPlan& p) {
-  if (m < 1 || m > SKINNY_MAX_M || k % BK || n % 4) return false;
-  p.mt = m <= 32 ? 1 : 2;
-  p.tiles = (n + 127) / 128;
+constexpr int SPLIT_TARGET_WG = 512;
+static int env_int(const char* name, int dflt) {
+  const char* f = getenv(name);
+  return f ? atoi(f) : dflt;
+}
+static bool split_plan(int m, int n, int k, SplitPlan& p) {
+  if (m < 1 || m > env_int("ORCA_SPLIT_MAX_M", SPLIT_MAX_M) || k % BK || n % 4) return false;
+  p.tile = m <= 32 ? 0 : m <= 64 ? 1 : 2;
+  const int bm = p.tile == 0 ? 32 : p.tile == 1 ? 64 : 128;
+  p.tiles = ((m + bm - 1) / bm) * ((n + 127) / 128);
+  const int target = std::max(1, env_int("ORCA_SPLIT_TARGET", SPLIT_TARGET_WG));
+  if (2 * p.tiles > target) return false;   // enough tiles already
   const int kt = k / BK;
-  int target = SKINNY_TARGET_WG;
-  if (const char* f = getenv("ORCA_SKINNY_TARGET")) target = std::max(1, atoi(f));
-  int splits = std::max(1, std::min({(target + p.tiles - 1) / p.tiles, SKINNY_MAX_SPLITS,
-                                     std::max(1, kt / 4)}));
+  const int splits = std::max(1, std::min({(target + p.tiles - 1) / p.tiles, SPLIT_MAX_SPLITS,
+                                           std::max(1, kt / 4)}));
   int per = (kt + splits - 1) / splits;
-  if (kt % 2 == 0) per += per & 1;   // even K steps per split: the two-step pipeline
+  if (kt % 2 == 0) per += per & 1;
   p.kt_per_split = per;
   p.splits = (kt + per - 1) / per;
-  return true;
+  return p.splits > 1;
 }
 
 size_t linear_workspace_bytes(int dtype, int m, int n, int k) {
-  SkinnyPlan p;
-  if (dtype != ORCA_BF16 || !skinny_plan(m, n, k, p)) return 0;
+  SplitPlan p;
+  if (dtype != ORCA_BF16 || !split_plan(m, n, k, p)) return 0;
   return (size_t)p.splits * m * n * sizeof(float);
 }
 
+template <int WGM, int WGN, int TI, int TJ>
+static void launch_partial(const SplitPlan& p, const void* a, const void* w, const EpiParams& pp,
+                           int m, int n, int k, hipStream_t s) {
+  if (p.kt_per_split % 2 == 0 && (k / BK) % 2 == 0)
+    launch_mfma<EPI_PARTIAL, WGM, WGN, TI, TJ, true>(a, w, nullptr, pp, m, n, k, s, p.splits,
+                                                     p.kt_per_split);
+  else
+    launch_mfma<EPI_PARTIAL, WGM, WGN, TI, TJ>(a, w, nullptr, pp, m, n, k, s, p.splits,
+                                               p.kt_per_split);
+}
+
 template <int EPI>
-static void launch_skinny(const SkinnyPlan& p, const void* a, const void* w, const void* bias,
-                          const EpiParams& ep, float* part, int m, int n, int k, hipStream_t s) {
+static void launch_split(const SplitPlan& p, const void* a, const void* w, const void* bias,
+                         const EpiParams& ep, float* part, int m, int n, int k, hipStream_t s) {
   EpiParams pp{};
   pp.out = part;
   pp.ldo = n;
-  const bool pipe = p.kt_per_split % 2 == 0 && (k / BK) % 2 == 0;
-  if (p.mt == 1) {
-    if (pipe) launch_mfma<EPI_PARTIAL, 1, 4, 1, 1, true>(a, w, bias, pp, m, n, k, s, p.splits, p.kt_per_split);
-    else launch_mfma<EPI_PARTIAL, 1, 4, 1, 1>(a, w, bias, pp, m, n, k, s, p.splits, p.kt_per_split);
-  } else {
-    if (pipe) launch_mfma<EPI_PARTIAL, 1, 4, 2, 1, true>(a, w, bias, pp, m, n, k, s, p.splits, p.kt_per_split);
-    else launch_mfma<EPI_PARTIAL, 1, 4, 2, 1>(a, w, bias, pp, m, n, k, s, p.splits, p.kt_per_split);
-  }
+  if (p.tile == 0) launch_partial<1, 4, 1, 1>(p, a, w, pp, m, n, k, s);
+  else if (p.tile == 1) launch_partial<1, 4, 2, 1>(p, a, w, pp, m, n, k, s);
+  else launch_partial<2, 2, 2, 2>(p, a, w, pp, m, n, k, s);
   const int threads = m * (n / 4);
   hipLaunchKernelGGL(skinny_reduce_kernel<EPI>, dim3((threads + 255) / 256), dim3(256), 0, s,
                      part, p.splits, (const bf16*)bias, ep, m, n);
@@ -461,11 +474,11 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
                          const EpiParams& ep, void* ws, size_t ws_bytes, int m, int n, int k,
                          hipStream_t s) {
   if (dtype == ORCA_BF16) {
-    SkinnyPlan sp;
+    SplitPlan sp;
     const int v = choose_variant(m, n);
-    if ((v == 10 || v < 0) && ws && skinny_plan(m, n, k, sp) &&
+    if ((v == 10 || v < 0) && ws && split_plan(m, n, k, sp) &&
         ws_bytes >= (size_t)sp.splits * m * n * sizeof(float)) {
-      launch_skinny<EPI>(sp, a, w, bias, ep, static_cast<float*>(ws), m, n, k, s);
+      launch_split<EPI>(sp, a, w, bias, ep, static_cast<float*>(ws), m, n, k, s);
       return;
     }
     switch (v) {
@@ -475,7 +488,7 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
         if ((k / BK) % 2 == 0) launch_mfma<EPI, 4, 2, 2, 4, true>(a, w, bias, ep, m, n, k, s);
         else launch_mfma<EPI, 4, 2, 2, 4>(a, w, bias, ep, m, n, k, s);
         break;
-      default:  // 7, and the few-rows choice when no workspace was given
+      default:  // 7, and the split-K choice when it does not apply
         if ((k / BK) % 2 == 0) launch_mfma<EPI, 2, 2, 2, 2, true>(a, w, bias, ep, m, n, k, s);
         else launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s);
         break;

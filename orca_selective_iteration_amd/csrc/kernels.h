@@ -27,12 +27,13 @@ struct QkvDest {
 constexpr int EPI_QKV = 3;
 // internal: fp32 partial sums of a K split, no bias (the few-rows path)
 constexpr int EPI_PARTIAL = 4;
-// bf16 problems with m <= SKINNY_MAX_M rows take a split-K weight-streaming
-// path when `ws` holds linear_workspace_bytes(dtype, m, n, k) bytes (fp32
-// partial sums); otherwise, and for every other shape, the tiled kernels
-// run and `ws` is not touched.
-constexpr int SKINNY_MAX_M = 64;
-constexpr int SKINNY_MAX_SPLITS = 16;
+// bf16 problems of at most SPLIT_MAX_M rows whose tiles are too few to fill
+// the GPU take a split-K path when `ws` holds
+// linear_workspace_bytes(dtype, m, n, k) bytes (fp32 partial sums);
+// otherwise, and for every other shape, the tiled kernels run and `ws` is
+// not touched.
+constexpr int SPLIT_MAX_M = 1024;
+constexpr int SPLIT_MAX_SPLITS = 16;
 size_t linear_workspace_bytes(int dtype, int m, int n, int k);
 hipError_t launch_linear(int dtype, int epilogue, const void* a, const void* w, const void* bias,
                          void* out, const QkvDest* qkv, int m, int n, int k, void* ws,

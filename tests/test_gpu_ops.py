@@ -64,10 +64,13 @@ LINEAR_CASES = [
     ("bf16", 1, 128, 64), ("bf16", 7, 192, 64), ("bf16", 130, 384, 256),
     ("bf16", 300, 1024, 1024), ("bf16", 257, 3072, 1024), ("bf16", 129, 128, 4096),
     ("f32", 7, 192, 64), ("f32", 65, 256, 128), ("f32", 1, 64, 64),
-    # few rows: the split-K weight-streaming path when a workspace is given
+    # few tiles: the split-K path when a workspace is given
     ("bf16", 33, 640, 2048), ("bf16", 64, 1536, 512), ("bf16", 31, 320, 4096),
-    ("bf16", 64, 128, 64),
+    ("bf16", 64, 128, 64), ("bf16", 200, 1280, 2048), ("bf16", 1000, 640, 1024),
 ]
+# shapes whose tiles are too few to fill the GPU: split-K must be taken
+SPLIT_EXPECTED = {(33, 640, 2048), (64, 1536, 512), (31, 320, 4096), (200, 1280, 2048),
+                  (1000, 640, 1024)}
 
 
 def _linear_case(dtype, m, n, k, epi, workspace):
@@ -101,8 +104,10 @@ def test_linear(dtype, m, n, k, epi, workspace):
     print(f"case linear {dtype} m={m} n={n} k={k} epi={epi} ws={workspace}", flush=True)
     got, ref, nb = _linear_case(dtype, m, n, k, epi, workspace)
     if workspace:
-        # bf16 with at most 64 rows is exactly the set that takes the split-K path
-        assert (nb > 0) == (dtype == "bf16" and m <= 64)
+        if dtype == "f32":
+            assert nb == 0
+        elif (m, n, k) in SPLIT_EXPECTED:
+            assert nb > 0
     assert np.isfinite(got).all()
     assert rel_err(got, ref) < TOL[dtype]
 
