@@ -39,7 +39,8 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                   choices=["tiny-fp32", "h1024-2l", "gpt13b-40l", "gpt175b-8l"])
+                   choices=["tiny-fp32", "h1024-2l", "gpt13b-40l", "gpt175b-8l",
+                            "gpt13b-40l-decode64"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--kernel-reps", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")

@@ -251,25 +251,35 @@ orca_status orca_op_attention(orca_ctx* ctx, int32_t layer, const orca_req_desc*
 
 /* ------------------------------------------------------------------------
  * Iteration-level scheduler ([houmin] 3.1.1; [0h-n0] scheduler algorithm;
- * [arcsin2] 4.2).  Host only.  Each step:
+ * [arcsin2] 4.2).  Host only.  Policies: 0 iteration-level, 1 request-level
+ * (static) baseline, 2 iteration-level with chunked prefill ([ultralytics]
+ * glossary, limits and combined techniques: long prompts are split so
+ * prefill does not stall decoding).  Each step:
  *   1. the batch returned by the previous step counts as executed: each
- *      member produced one token, its kv_len grew by its q_len;
- *   2. finished requests (generated == out_len) leave and their K/V
- *      reservation is released at once (policy 1: only when every member
- *      of the running batch has finished);
+ *      member's kv_len grew by its q_len, and a member whose prompt is then
+ *      complete produced one token (a prompt's last chunk yields its first
+ *      token);
+ *   2. finished (generated == out_len) and cancelled requests leave and
+ *      their K/V reservation is released at once (policy 1: a finished
+ *      member only when every member of the running batch is through);
  *   3. requests with arrival <= now join the FCFS queue;
- *   4. FCFS admission while the batch has fewer than max_batch requests:
- *      the head is admitted if the batch's rows (1 per continuing request +
- *      the prompts admitted so far + its prompt) stay <= token_budget, its
- *      reservation prompt_len + max_tokens fits the free slot count, and a
- *      contiguous range exists; the first miss ends admission (no skipping);
- *      policy 1 admits only when no batch is running;
- *   5. the batch is emitted: continuing requests (increment, admission
- *      order), then this step's admissions (initiation).
+ *   4. rows already committed: one per decoding request, then (policy 2)
+ *      the next chunk of each prompt still being prefilled, as much as the
+ *      token budget leaves, in admission order;
+ *   5. FCFS admission while the batch has fewer than max_batch requests:
+ *      the head is admitted if its reservation prompt_len + max_tokens fits
+ *      the free slot count and a contiguous range exists, and if its prompt
+ *      fits the budget left (policy 2: if any budget is left; its first
+ *      chunk takes what is left); the first miss ends admission (no
+ *      skipping); policy 1 admits only when no batch is running;
+ *   6. the batch is emitted: decoding requests (increment, admission
+ *      order), continuing prompt chunks, then this step's admissions
+ *      (initiation; a chunk after the first has kv_len = prompt tokens
+ *      already cached).
  * ---------------------------------------------------------------------- */
 typedef struct orca_sched orca_sched;
 
-enum { ORCA_POLICY_ITERATION = 0, ORCA_POLICY_STATIC = 1 };
+enum { ORCA_POLICY_ITERATION = 0, ORCA_POLICY_STATIC = 1, ORCA_POLICY_CHUNKED = 2 };
 
 /* kv: the allocator reservations come from (borrowed); its capacity is the
  * scheduler's K/V slot budget. */
@@ -280,7 +290,8 @@ void        orca_sched_destroy(orca_sched* s);
 /* Queue a request.  out_len is the output length (the request finishes
  * after producing out_len tokens; the policy never reads it ahead of time).
  * ORCA_ERR_INVALID if the id is taken, a length is < 1, out_len > max_tokens,
- * prompt_len > token_budget or prompt_len + max_tokens > the K/V capacity. */
+ * prompt_len > token_budget (policies 0 and 1) or prompt_len + max_tokens >
+ * the K/V capacity. */
 orca_status orca_sched_submit(orca_sched* s, int64_t id, double arrival, int32_t prompt_len,
                               int32_t max_tokens, int32_t out_len);
 
@@ -289,6 +300,14 @@ orca_status orca_sched_submit(orca_sched* s, int64_t id, double arrival, int32_t
  * ORCA_ERR_INVALID if cap < max_batch. */
 orca_status orca_sched_step(orca_sched* s, double now, orca_req_desc* out, int64_t* out_ids,
                             int32_t cap, int32_t* n_out);
+
+/* Withdraw a request ([houmin] 3.1.1, scheduling workflow: a cancelled
+ * request should leave the batch promptly and free its memory).  A queued
+ * request is dropped at once; an admitted one leaves at the next step's
+ * eviction (so a batch the engine may still be running is unaffected) and
+ * its K/V reservation is released there.  ORCA_ERR_INVALID for an unknown,
+ * already released or already cancelled id. */
+orca_status orca_sched_cancel(orca_sched* s, int64_t id);
 
 /* 1 when nothing is queued, waiting or running. */
 int32_t orca_sched_idle(const orca_sched* s);

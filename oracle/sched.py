@@ -24,6 +24,12 @@ Sources:
              continuous 50 steps / 78% busy).
   [estelledc] estelledc.github.io Orca notes, case 1: A=100, B=10, C=50 on
              three slots; D joins at step 11, E at 51, F at 101.
+  [houmin-cancel] garden.houmin.site/infra/orca 3.1.1, scheduling workflow:
+             Orca leaves cancelled requests unhandled; they should leave the
+             batch promptly and their memory be released.
+  [ultralytics-chunk] ultralytics.com glossary "Continuous Batching", limits
+             and combined techniques: chunked prefill splits long prompts so
+             a newcomer's prefill does not stall the others' decoding.
 
 Readings where the pages leave a step open:
   * release exactly what was reserved (prompt + max_tokens); the digest's
@@ -41,7 +47,23 @@ Readings where the pages leave a step open:
     holds none; members that finished keep their slot idle (not computed)
     until the last member finishes, then all are released together;
   * time is an explicit argument: step(now) admits requests with
-    arrival <= now.
+    arrival <= now;
+  * cancel(id) drops a queued request at once; an admitted one leaves at the
+    next step's eviction like a finished one (K/V released then, under every
+    policy), so the batch the engine may still be running is never changed
+    under it;
+  * "chunked" policy (iteration-level with chunked prefill): a prompt is
+    split across iterations so every batch fills the token budget; rows are
+    ordered increments, then continuing prompt chunks, then this step's
+    admissions (each group in admission order); a continuing prompt takes
+    what the budget leaves after the increments, in admission order; a new
+    request is admitted while any budget is left (its first chunk may be a
+    single token), the K/V checks and the break on a miss unchanged; a chunk
+    after the first is an initiation whose kv_len is the prompt tokens
+    already cached; a prompt longer than the budget is accepted;
+  * one accounting rule for every policy: after an iteration a member's
+    kv_len grows by its q_len, and it has produced a token iff its prompt is
+    then complete (its first token comes with its last prompt chunk).
 """
 from __future__ import annotations
 
@@ -111,6 +133,7 @@ class Request:
     admitted_at: int = -1   # iteration index (0-based) of its initiation
     finished_at: int = -1   # iteration index that produced its last token
     released_at: int = -1   # iteration index at whose start it was evicted
+    cancelled: bool = False
 
     @property
     def reserved(self) -> int:
@@ -119,6 +142,15 @@ class Request:
     @property
     def done(self) -> bool:
         return self.generated >= self.out_len
+
+    @property
+    def prefilled(self) -> bool:
+        return self.kv_len >= self.prompt_len
+
+    @property
+    def gone(self) -> bool:
+        """Nothing left to compute: finished or cancelled."""
+        return self.done or self.cancelled
 
 
 @dataclass(frozen=True)
@@ -142,7 +174,7 @@ class Scheduler:
 
     def __init__(self, max_batch: int, token_budget: int, kv_slots: int,
                  policy: str = "iteration"):
-        assert policy in ("iteration", "static")
+        assert policy in ("iteration", "static", "chunked")
         assert max_batch >= 1 and token_budget >= 1 and kv_slots >= 0
         self.max_batch = max_batch
         self.token_budget = token_budget
@@ -165,28 +197,53 @@ class Scheduler:
             return False
         if out_len < 1 or out_len > max_tokens:
             return False
-        if prompt_len > self.token_budget or prompt_len + max_tokens > self.kv_slots:
+        if prompt_len + max_tokens > self.kv_slots:
+            return False
+        if self.policy != "chunked" and prompt_len > self.token_budget:
             return False
         r = Request(rid, arrival, prompt_len, max_tokens, out_len)
         self.requests[rid] = r
         heapq.heappush(self.pending, (arrival, rid, r))
         return True
 
+    # ------------------------------------------------------------------ cancel
+    def cancel(self, rid: int) -> bool:
+        """Withdraw a request ([houmin-cancel]).  False if it is unknown,
+        already released or already cancelled."""
+        r = self.requests.get(rid)
+        if r is None or r.cancelled or r.released_at >= 0:
+            return False
+        if r.admitted_at < 0:                    # still queued: drop it now
+            r.cancelled = True
+            if r in self.waiting:
+                self.waiting.remove(r)
+            else:
+                self.pending = [e for e in self.pending if e[2] is not r]
+                heapq.heapify(self.pending)
+            return True
+        r.cancelled = True                       # admitted: leaves at the next step
+        return True
+
     # -------------------------------------------------------------------- step
     def step(self, now: float) -> List[BatchEntry]:
-        # the previous batch has run: one token each, K/V grew by q_len
+        # the previous batch has run: K/V grew by q_len; a member whose prompt
+        # is now complete produced one token
         for r, q_len in self.last:
-            r.generated += 1
             r.kv_len += q_len
-            if r.done:
-                r.finished_at = self.iteration - 1
+            if r.prefilled:
+                r.generated += 1
+                if r.done:
+                    r.finished_at = self.iteration - 1
         self.last = []
 
-        # 1. evict finished requests, release their K/V at once ([houmin] 3.1.1)
-        if self.policy == "iteration":
-            leaving = [r for r in self.active if r.done]
+        # 1. evict finished and cancelled requests, release their K/V at once
+        #    ([houmin] 3.1.1); the static policy keeps finished members until
+        #    the whole batch is through
+        if self.policy == "static":
+            whole = all(r.gone for r in self.active)
+            leaving = [r for r in self.active if r.cancelled or whole]
         else:
-            leaving = list(self.active) if all(r.done for r in self.active) else []
+            leaving = [r for r in self.active if r.gone]
         for r in leaving:
             self.alloc.free(r.kv_base)
             self.used -= r.reserved
@@ -197,17 +254,31 @@ class Scheduler:
         while self.pending and self.pending[0][0] <= now:
             self.waiting.append(heapq.heappop(self.pending)[2])
 
-        # 3. rows already committed: one per continuing (unfinished) request
-        running = [r for r in self.active if not r.done]
+        # 3. rows already committed: one per decoding request, then the
+        #    chunks of prompts still being prefilled (chunked policy)
+        running = [r for r in self.active if not r.gone and r.prefilled]
         tok = len(running)
+        chunks: List[Tuple[Request, int]] = []
+        for r in self.active:
+            if not r.gone and not r.prefilled:
+                q = min(r.prompt_len - r.kv_len, self.token_budget - tok)
+                if q > 0:
+                    chunks.append((r, q))
+                    tok += q
 
         # 4. FCFS admission, stop at the first miss ([0h-n0] scheduler algorithm)
-        admitted: List[Request] = []
-        if self.policy == "iteration" or not self.active:
+        admitted: List[Tuple[Request, int]] = []
+        if self.policy != "static" or not self.active:
             while self.waiting and len(self.active) + len(admitted) < self.max_batch:
                 c = self.waiting[0]
-                if tok + c.prompt_len > self.token_budget:
-                    break
+                if self.policy == "chunked":
+                    q = min(c.prompt_len, self.token_budget - tok)
+                    if q <= 0:
+                        break
+                else:
+                    q = c.prompt_len
+                    if tok + q > self.token_budget:
+                        break
                 if self.used + c.reserved > self.kv_slots:
                     break
                 base = self.alloc.alloc(c.reserved)
@@ -217,21 +288,22 @@ class Scheduler:
                 c.kv_base = base
                 c.admitted_at = self.iteration
                 self.used += c.reserved
-                tok += c.prompt_len
-                admitted.append(c)
-        self.active.extend(admitted)
+                tok += q
+                admitted.append((c, q))
+        self.active.extend(c for c, _ in admitted)
 
-        # 5. emit: increments (admission order) then this step's initiations
+        # 5. emit: increments (admission order), continuing prompt chunks, then
+        #    this step's initiations
         batch: List[BatchEntry] = []
         off = 0
         for r in running:
             batch.append(BatchEntry(r.id, off, 1, r.kv_len, INCREMENT, r.kv_base))
             self.last.append((r, 1))
             off += 1
-        for r in admitted:
-            batch.append(BatchEntry(r.id, off, r.prompt_len, 0, INITIATION, r.kv_base))
-            self.last.append((r, r.prompt_len))
-            off += r.prompt_len
+        for r, q in chunks + admitted:
+            batch.append(BatchEntry(r.id, off, q, r.kv_len, INITIATION, r.kv_base))
+            self.last.append((r, q))
+            off += q
         if batch:
             self.iteration += 1
         return batch

@@ -210,9 +210,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   const int half = lane >> 5, col = lane & 31;
   const size_t H = (size_t)a.hidden;
 
-  // this lane's query: position qpos of the prompt (kv_len is 0)
-  const int qpos = it.q0 + w * 32 + col;
-  const int qrow = rq.q_offset + min(qpos, it.q1 - 1);
+  // this lane's query: row qi of the prompt chunk, at absolute position
+  // qpos = kv_len + qi (kv_len: prompt tokens cached by earlier chunks)
+  const int qi = it.q0 + w * 32 + col;
+  const int qpos = rq.kv_len + qi;
+  const int qrow = rq.q_offset + min(qi, it.q1 - 1);
   bf16x8_t qf[D / 16];
   {
     const bf16* qp = (const bf16*)a.q + (size_t)qrow * H + h * D + half * 8;
@@ -227,8 +229,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   float m_run = NEG_BIG, l_run = 0.f;
   const float sc = LOG2E / sqrtf((float)D);
 
-  const int kend = min(it.q1, it.q0 + BQ);              // keys the block needs
-  const int kend_wave = min(it.q1, it.q0 + w * 32 + 32);  // keys this wave needs
+  // keys the block needs, and this wave (absolute positions, exclusive)
+  const int kend = rq.kv_len + min(it.q1, it.q0 + BQ);
+  const int kend_wave = rq.kv_len + min(it.q1, it.q0 + w * 32 + 32);
   const size_t head_base = ((size_t)h * a.cap + (size_t)rq.kv_base) * D;
   const bf16* kb = (const bf16*)a.k_pool + head_base;
   const bf16* vb = (const bf16*)a.v_pool + head_base;

@@ -100,10 +100,7 @@ orca_status validate(orca_ctx* c, const orca_req_desc* reqs, int32_t n, int32_t*
                    r.q_offset, (long long)off);
     ORCA_CHECK_ARG(r.q_len >= 1, "request %d: q_len %d < 1", i, r.q_len);
     ORCA_CHECK_ARG(r.kv_len >= 0, "request %d: kv_len %d < 0", i, r.kv_len);
-    if (r.phase == ORCA_INITIATION) {
-      ORCA_CHECK_ARG(r.kv_len == 0, "request %d: initiation with kv_len %d (a request with a "
-                     "cache is in the increment phase)", i, r.kv_len);
-    } else {
+    if (r.phase != ORCA_INITIATION) {
       ORCA_CHECK_ARG(r.phase == ORCA_INCREMENT, "request %d: unknown phase %d", i, r.phase);
       ORCA_CHECK_ARG(r.kv_len >= 1, "request %d: increment without a cache", i);
       ORCA_CHECK_ARG(r.q_len == 1, "request %d: increment with q_len %d", i, r.q_len);
@@ -184,10 +181,13 @@ void build_plan(const orca_ctx* c, const orca_req_desc* reqs, int32_t n, int32_t
   p.n_items = ni;
   p.n_srows = ns;
   p.n_pf = np;
-  // causal prefill tiles cost ~ their last query position: dispatch the
-  // longest first so the short ones fill in behind them
-  std::sort(p.pf, p.pf + np, [](const PrefillItem& a, const PrefillItem& b) {
-    return a.q1 != b.q1 ? a.q1 > b.q1 : a.req < b.req;
+  // causal prefill tiles cost ~ their last key position (cached prefix +
+  // last query): dispatch the longest first so the short ones fill in
+  // behind them
+  const DevReq* dr = p.reqs;
+  std::sort(p.pf, p.pf + np, [dr](const PrefillItem& a, const PrefillItem& b) {
+    const int64_t ea = int64_t(dr[a.req].kv_len) + a.q1, eb = int64_t(dr[b.req].kv_len) + b.q1;
+    return ea != eb ? ea > eb : (a.req != b.req ? a.req < b.req : a.q0 < b.q0);
   });
 }
 
@@ -279,11 +279,14 @@ orca_status orca_create(const orca_model_desc* desc, const orca_layer_weights* l
   c->kv = kv;
   c->max_rows = max_rows;
   c->max_reqs = max_reqs;
-  // split-KV items: every row yields at most 1 + keys / SPLIT_CHUNK; the
-  // keys of increment rows lie in disjoint pool ranges; fp32 initiation
-  // rows of one prompt add a triangle (bounded by max_rows^2 / 2)
+  // split-KV items: a row with `keys` keys yields ceil(keys / SPLIT_CHUNK).
+  // bf16: only increment rows take this path, one per request over disjoint
+  // pool ranges, so the keys of all of them add up to at most the capacity.
+  // fp32: every row does, and the rows of one prompt chunk share a range;
+  // each row has at most min(capacity, max_rows + its cached prefix) keys.
   c->max_items = int64_t(max_rows) + d.kv_capacity / SPLIT_CHUNK + 1;
-  if (d.dtype == ORCA_F32) c->max_items += (int64_t(max_rows) * max_rows / 2) / SPLIT_CHUNK + max_rows;
+  if (d.dtype == ORCA_F32)
+    c->max_items = int64_t(max_rows) * (1 + d.kv_capacity / SPLIT_CHUNK) + 1;
   c->max_pf = d.dtype == ORCA_BF16 ? int64_t(max_rows) / PREFILL_ROWS + max_reqs : 0;
   const size_t R = max_rows, H = d.hidden, F = d.ffn, s = dsize(d.dtype);
   size_t o = 0;

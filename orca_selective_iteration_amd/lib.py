@@ -25,7 +25,7 @@ ORCA_OK, ORCA_ERR_INVALID, ORCA_ERR_NOSPACE, ORCA_ERR_HIP, ORCA_ERR_UNSUPPORTED 
 ORCA_F32, ORCA_BF16 = 0, 1
 ORCA_INITIATION, ORCA_INCREMENT = 0, 1
 ORCA_EPI_BIAS, ORCA_EPI_BIAS_GELU, ORCA_EPI_BIAS_RESID = 0, 1, 2
-ORCA_POLICY_ITERATION, ORCA_POLICY_STATIC = 0, 1
+ORCA_POLICY_ITERATION, ORCA_POLICY_STATIC, ORCA_POLICY_CHUNKED = 0, 1, 2
 
 LAYER_KEYS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
               "ln2_g", "ln2_b", "w_1", "b_1", "w_2", "b_2")
@@ -85,6 +85,7 @@ def _declare(lib):
         "orca_sched_submit": (c_int32, [V, I64, c_double, I32, I32, I32]),
         "orca_sched_step": (c_int32, [V, c_double, POINTER(orca_req_desc), POINTER(I64), I32,
                                       POINTER(I32)]),
+        "orca_sched_cancel": (c_int32, [V, I64]),
         "orca_sched_idle": (I32, [V]),
         "orca_sched_next_arrival": (c_int32, [V, POINTER(c_double)]),
         "orca_sched_request_info": (c_int32, [V, I64, POINTER(I64), POINTER(I64), POINTER(I64)]),
@@ -280,6 +281,10 @@ def orca_sched_step(s: int, now: float, cap: int):
     n = c_int32()
     _check(load().orca_sched_step(s, now, out, ids, cap, byref(n)), "orca_sched_step")
     return [out[i] for i in range(n.value)], [ids[i] for i in range(n.value)]
+
+
+def orca_sched_cancel(s: int, rid: int) -> None:
+    _check(load().orca_sched_cancel(s, rid), "orca_sched_cancel")
 
 
 def orca_sched_idle(s: int) -> bool:

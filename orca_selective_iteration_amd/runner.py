@@ -122,7 +122,9 @@ class DeviceModel:
         kv_len = kv_len or [w.kv_len[i] for i in idx]
         out, off = [], 0
         for i, q, kv in zip(idx, q_len, kv_len):
-            phase = L.ORCA_INITIATION if kv == 0 else L.ORCA_INCREMENT
+            # one new token over a cache: increment; otherwise a prompt or a
+            # prompt chunk over the tokens earlier chunks cached
+            phase = L.ORCA_INCREMENT if (kv > 0 and q == 1) else L.ORCA_INITIATION
             out.append((off, q, kv, phase, self.bases[i]))
             off += q
         return out

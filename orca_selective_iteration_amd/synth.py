@@ -20,6 +20,11 @@ Workloads (all parameters random-init, no trained weights exist here):
   gpt175b-8l     GPT-3-175B layer shape: 8 layers, H=12288, 96 heads,
                  FFN 49152, bf16.  8 initiations with prompts U[128,1024] and
                  248 increments with K/V lengths U[512,2048].
+  gpt13b-40l-decode64
+                 the 13B shape with the steady-state batch of a serving trace
+                 at a full 64-request batch: 64 increments, no initiation,
+                 K/V lengths U[32,1024] (prompt U[32,512] plus up to 512
+                 generated tokens).
 
 Draw order for one seed (numpy PCG64, ``default_rng(seed)``): prompt lengths,
 then K/V lengths; then for every layer ln1_g, ln1_b, W_qkv, b_qkv, W_o, b_o,
@@ -54,6 +59,7 @@ MODELS: Dict[str, dict] = {
     "h1024-2l": dict(layers=2, hidden=1024, heads=16, ffn=4096, dtype="bf16"),
     "gpt13b-40l": dict(layers=40, hidden=5120, heads=40, ffn=20480, dtype="bf16"),
     "gpt175b-8l": dict(layers=8, hidden=12288, heads=96, ffn=49152, dtype="bf16"),
+    "gpt13b-40l-decode64": dict(layers=40, hidden=5120, heads=40, ffn=20480, dtype="bf16"),
 }
 
 LN_EPS = 1e-5
@@ -110,6 +116,9 @@ def _lengths(name: str, rng: np.random.Generator) -> Tuple[List[int], List[int]]
     elif name == "gpt175b-8l":
         prompts = rng.integers(128, 1024, size=8, endpoint=True)
         kvs = rng.integers(512, 2048, size=248, endpoint=True)
+    elif name == "gpt13b-40l-decode64":
+        prompts = np.zeros(0, dtype=np.int64)
+        kvs = rng.integers(32, 1024, size=64, endpoint=True)
     else:
         raise KeyError(name)
     q = [1] * len(kvs) + [int(p) for p in prompts]

@@ -33,6 +33,10 @@ from . import lib as L
 from . import synth
 
 
+POLICY_NAMES = {L.ORCA_POLICY_ITERATION: "iteration", L.ORCA_POLICY_STATIC: "static",
+                L.ORCA_POLICY_CHUNKED: "chunked"}
+
+
 class TraceEngine:
     """Weights, an HBM-sized K/V pool and one engine context."""
 
@@ -119,7 +123,7 @@ class TraceEngine:
                 adm, fin, _ = L.orca_sched_request_info(s, r.id)
                 if policy == L.ORCA_POLICY_STATIC:
                     # request-level: the response leaves with the whole batch
-                    _, _, rel = L.orca_sched_request_info(s, r.id)
+                    rel = L.orca_sched_request_info(s, r.id)[2]
                     t_end = steps[rel][0] if rel < len(steps) else wall
                 else:
                     t_end = iter_end[fin]
@@ -127,7 +131,7 @@ class TraceEngine:
             gen = sum(r.out_len for r in requests)
             lats = np.array(lats)
             return {
-                "policy": "iteration" if policy == L.ORCA_POLICY_ITERATION else "static",
+                "policy": POLICY_NAMES[policy],
                 "wall_s": round(wall, 3), "iterations": iters, "rows_processed": rows,
                 "generated_tokens": gen,
                 "generated_tokens_per_s": round(gen / wall, 1),
@@ -159,7 +163,8 @@ def main(argv=None):
     p.add_argument("--rate", type=float, default=32.0, help="arrivals per second (inf: all at 0)")
     p.add_argument("--max-batch", type=int, default=64)
     p.add_argument("--token-budget", type=int, default=4096)
-    p.add_argument("--policy", choices=["both", "iteration", "static"], default="both")
+    p.add_argument("--policy", choices=["both", "iteration", "static", "chunked", "all"],
+                   default="both", help="both: iteration and static; all: the three")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--log", default=None, help="write the per-step (now, ids) log as JSON")
     p.add_argument("--max-wall", type=float, default=600.0)
@@ -177,10 +182,11 @@ def main(argv=None):
         warm = [synth.TraceRequest(10**9, 0.0, 64, 8, 2)]
         eng.run(warm, a.max_batch, a.token_budget, L.ORCA_POLICY_ITERATION)
         pols = {"both": [L.ORCA_POLICY_ITERATION, L.ORCA_POLICY_STATIC],
-                "iteration": [L.ORCA_POLICY_ITERATION], "static": [L.ORCA_POLICY_STATIC]}[a.policy]
+                "all": [L.ORCA_POLICY_ITERATION, L.ORCA_POLICY_CHUNKED, L.ORCA_POLICY_STATIC],
+                "iteration": [L.ORCA_POLICY_ITERATION], "static": [L.ORCA_POLICY_STATIC],
+                "chunked": [L.ORCA_POLICY_CHUNKED]}[a.policy]
         for pol in pols:
-            log(f"policy {'iteration' if pol == 0 else 'static'}: {a.requests} requests at "
-                f"{a.rate}/s")
+            log(f"policy {POLICY_NAMES[pol]}: {a.requests} requests at {a.rate}/s")
             res = eng.run(reqs, a.max_batch, a.token_budget, pol, log=log, max_wall=a.max_wall)
             res.pop("steps")
             calls = res.pop("calls")

@@ -69,10 +69,17 @@ def test_allocator_errors():
 
 # ------------------------------------------------------------------ scheduler
 
-def replay_both(reqs, max_batch, budget, kv_slots, policy, dt=1.0):
+POLICIES = {"iteration": L.ORCA_POLICY_ITERATION, "static": L.ORCA_POLICY_STATIC,
+            "chunked": L.ORCA_POLICY_CHUNKED}
+
+
+def replay_both(reqs, max_batch, budget, kv_slots, policy, dt=1.0, cancels=None):
     """Drive the native and the oracle scheduler with the same clock; assert
-    identical batches at every step; return the oracle result."""
-    pol = L.ORCA_POLICY_ITERATION if policy == "iteration" else L.ORCA_POLICY_STATIC
+    identical batches at every step; return the oracle result.  cancels maps
+    a step index (steps taken so far, empty ones included) to the ids
+    withdrawn just before that step."""
+    pol = POLICIES[policy]
+    cancels = cancels or {}
     kv = L.orca_kv_create(kv_slots)
     s = L.orca_sched_create(kv, max_batch, budget, pol)
     o = osch.Scheduler(max_batch, budget, kv_slots, policy)
@@ -84,8 +91,15 @@ def replay_both(reqs, max_batch, budget, kv_slots, policy, dt=1.0):
             else:
                 with pytest.raises(L.OrcaError):
                     L.orca_sched_submit(s, rid, arr, prompt, mt, out)
-        now, steps = 0.0, 0
+        now, steps, calls = 0.0, 0, 0
         while True:
+            for rid in cancels.get(calls, ()):
+                if o.cancel(rid):
+                    L.orca_sched_cancel(s, rid)
+                else:
+                    with pytest.raises(L.OrcaError):
+                        L.orca_sched_cancel(s, rid)
+            calls += 1
             want = o.step(now)
             got, ids = L.orca_sched_step(s, now, max_batch)
             assert ids == [e.id for e in want]
@@ -125,7 +139,7 @@ def test_native_scheduler_page_examples():
     assert [o.requests[i].admitted_at + 1 for i in (3, 4, 5)] == [11, 51, 101]
 
 
-@pytest.mark.parametrize("policy", ["iteration", "static"])
+@pytest.mark.parametrize("policy", ["iteration", "static", "chunked"])
 @pytest.mark.parametrize("seed", range(8))
 def test_native_scheduler_matches_oracle_random(policy, seed):
     rng = np.random.default_rng(200 + seed)
@@ -140,9 +154,30 @@ def test_native_scheduler_matches_oracle_random(policy, seed):
     reqs.append((n, 1.0, 500, 10, 5))            # longer than the budget: rejected
     reqs.append((n + 1, 1.0, 5, 10, 11))         # out_len > max_tokens: rejected
     max_batch = int(rng.integers(1, 9))
-    budget = int(rng.integers(40, 120))
+    budget = int(rng.integers(40, 120)) if policy != "chunked" else int(rng.integers(4, 50))
     kv = int(rng.integers(80, 400))
+    if policy == "chunked":
+        reqs.append((n + 2, 2.0, 300, 10, 5))    # prompt far above the budget: chunked
     replay_both(reqs, max_batch, budget, kv, policy, dt=float(rng.uniform(0.2, 2.0)))
+
+
+@pytest.mark.parametrize("policy", ["iteration", "static", "chunked"])
+@pytest.mark.parametrize("seed", range(6))
+def test_native_scheduler_cancel_matches_oracle(policy, seed):
+    rng = np.random.default_rng(900 + seed)
+    n = 50
+    arr = np.cumsum(rng.exponential(1.0, size=n))
+    reqs = []
+    for i in range(n):
+        mt = int(rng.integers(1, 30))
+        reqs.append((i, float(arr[i]), int(rng.integers(1, 40)), mt, int(rng.integers(1, mt + 1))))
+    # withdraw random ids at random steps: queued, running, finished, twice, unknown
+    cancels = {}
+    for _ in range(40):
+        cancels.setdefault(int(rng.integers(0, 120)), []).append(int(rng.integers(0, n + 3)))
+    budget = int(rng.integers(40, 120)) if policy != "chunked" else int(rng.integers(4, 50))
+    replay_both(reqs, int(rng.integers(1, 9)), budget, int(rng.integers(80, 400)), policy,
+                dt=float(rng.uniform(0.2, 2.0)), cancels=cancels)
 
 
 def test_scheduler_argument_errors():
@@ -158,6 +193,16 @@ def test_scheduler_argument_errors():
             L.orca_sched_submit(s, 1, 0.0, 3, 5, 5)       # duplicate id
         with pytest.raises(L.OrcaError):
             L.orca_sched_step(s, 0.0, 3)                   # cap < max_batch
+        with pytest.raises(L.OrcaError):
+            L.orca_sched_submit(s, 2, 0.0, 11, 5, 5)       # prompt above the budget
+        with pytest.raises(L.OrcaError):
+            L.orca_sched_cancel(s, 99)                     # unknown id
+        L.orca_sched_cancel(s, 1)
+        with pytest.raises(L.OrcaError):
+            L.orca_sched_cancel(s, 1)                      # twice
+        L.orca_sched_destroy(s)
+        s = L.orca_sched_create(kv, 4, 10, L.ORCA_POLICY_CHUNKED)
+        L.orca_sched_submit(s, 2, 0.0, 11, 5, 5)           # chunked: accepted
         L.orca_sched_destroy(s)
     finally:
         L.orca_kv_destroy(kv)

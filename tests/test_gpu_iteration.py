@@ -74,6 +74,11 @@ def test_h1024_two_layer_bf16():
     (3, 512, 8, 1024, "bf16", [1, 1, 129, 1, 64, 1], [700, 2, 0, 1025, 0, 1]),
     (1, 256, 2, 256, "bf16", [300], [0]),
     (2, 128, 2, 256, "bf16", [1] * 40, list(range(1, 41))),
+    # prompt chunks over a cached prefix (chunked prefill), beside increments
+    # and a whole prompt: prefill tiles with the key range shifted by kv_len
+    (2, 512, 4, 1024, "bf16", [1, 200, 1, 77, 50], [300, 130, 5, 1000, 0]),
+    (1, 256, 2, 512, "bf16", [129, 1, 255], [1, 64, 513]),
+    (2, 256, 2, 512, "f32", [1, 40, 3, 17], [50, 70, 600, 0]),
 ])
 def test_custom_mixed_batches(layers, hidden, heads, ffn, dtype, q, kv):
     print(f"case custom {layers} {hidden} {heads} {dtype} n={len(q)}", flush=True)
@@ -131,6 +136,36 @@ def test_prefix_invariance_on_gpu():
         model.close()
 
 
+def test_chunked_prompt_on_gpu():
+    """A prompt run as three chunks (each an initiation over what the earlier
+    chunks cached) gives the rows and K/V of the whole prompt in one
+    initiation (oracle), with a decoding request sharing every batch."""
+    print("case chunked prompt", flush=True)
+    P, cuts = 300, [0, 100, 250, 300]
+    work = synth.custom_workload(2, 256, 2, 512, "bf16", [1, P], [40, 0])
+    hin = synth.host_inputs(work, 8)
+    model = DeviceModel(work, host=hin, device=DEV)
+    try:
+        yr, app = om.selective_iteration(f64_params(hin.params), oracle_reqs(work),
+                                         hin.x.astype(np.float64), f64_caches(hin.caches),
+                                         work.heads, work.eps)
+        b0, b1 = model.bases
+        parts = []
+        for c0, c1 in zip(cuts[:-1], cuts[1:]):
+            # the decoding request repeats its own step (same row, same slot)
+            d = [(0, 1, 40, L.ORCA_INCREMENT, b0), (1, c1 - c0, c0, L.ORCA_INITIATION, b1)]
+            y = run_gpu(model, work, np.concatenate([hin.x[:1], hin.x[1 + c0:1 + c1]]), d)
+            assert rel_err(y[:1], yr[:1]) < TOL["bf16"]
+            parts.append(y[1:])
+        assert rel_err(np.concatenate(parts), yr[1:]) < TOL["bf16"]
+        for l in range(work.layers):
+            k, v = model.cache_rows(l, 1, 0, P)
+            assert rel_err(k, app[l][1][0]) < TOL["bf16"]
+            assert rel_err(v, app[l][1][1]) < TOL["bf16"]
+    finally:
+        model.close()
+
+
 def test_empty_batch_and_invalid_descriptors():
     print("case errors", flush=True)
     work = synth.custom_workload(1, 128, 2, 256, "bf16", [1, 3], [4, 0])
@@ -145,7 +180,6 @@ def test_empty_batch_and_invalid_descriptors():
             [good[0], (2, 3, 0, L.ORCA_INITIATION, good[1][4])],      # offset gap
             [(0, 2, 4, L.ORCA_INCREMENT, good[0][4]), good[1]],       # increment q_len 2
             [(0, 1, 0, L.ORCA_INCREMENT, good[0][4]), good[1]],       # increment w/o cache
-            [good[0], (1, 3, 1, L.ORCA_INITIATION, good[1][4])],      # initiation with cache
             [good[0], (1, 3, 0, L.ORCA_INITIATION, good[0][4])],      # overlapping slots
             [good[0], (1, 3, 0, L.ORCA_INITIATION, 10**6)],           # outside the pool
             [good[0], (1, 3, 0, L.ORCA_INITIATION, good[1][4] + 1)],  # outside reservation

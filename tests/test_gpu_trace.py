@@ -12,19 +12,24 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("policy", [L.ORCA_POLICY_ITERATION, L.ORCA_POLICY_STATIC])
+NAMES = {L.ORCA_POLICY_ITERATION: "iteration", L.ORCA_POLICY_STATIC: "static",
+         L.ORCA_POLICY_CHUNKED: "chunked"}
+
+
+@pytest.mark.parametrize("policy", [L.ORCA_POLICY_ITERATION, L.ORCA_POLICY_STATIC,
+                                    L.ORCA_POLICY_CHUNKED])
 def test_trace_replays_through_the_oracle(policy):
     print(f"case trace policy={policy}", flush=True)
     work = synth.custom_workload(2, 256, 2, 512, "bf16", [1], [0])
     reqs = synth.poisson_trace(60, 400.0, seed=3, prompt=(4, 60), out=(1, 24), max_tokens=24)
-    max_batch, budget = 8, 128
+    # chunked prefill: a budget below the longest prompt, so prompts split
+    max_batch, budget = 8, (128 if policy != L.ORCA_POLICY_CHUNKED else 40)
     eng = TraceEngine(work, max_batch, budget, kv_slots=4000)
     try:
         res = eng.run(reqs, max_batch, budget, policy)
     finally:
         eng.close()
-    o = osch.Scheduler(max_batch, budget, 4000,
-                       "iteration" if policy == L.ORCA_POLICY_ITERATION else "static")
+    o = osch.Scheduler(max_batch, budget, 4000, NAMES[policy])
     for r in reqs:
         assert o.submit(r.id, r.arrival, r.prompt_len, r.max_tokens, r.out_len)
     for now, ids in res["calls"]:

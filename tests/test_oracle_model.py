@@ -246,6 +246,39 @@ def test_prefix_invariance(split):
         assert rel_err(cache[l][0][1], app_full[l][0][1]) < 1e-12
 
 
+@pytest.mark.parametrize("cuts", [(3,), (1, 4), (2, 3, 6), (7,)])
+def test_chunked_prompt_equals_whole_prompt(cuts):
+    """A prompt run as consecutive chunks (each chunk an initiation over the
+    K/V its predecessors appended, rows at absolute positions kv_len + j)
+    gives the rows and K/V of the whole prompt in one initiation; a second
+    request in the same batches must not notice."""
+    P, layers, H = 8, 2, 32
+    w = synth.custom_workload(layers, H, 4, 64, "f32", [P, 5], [0, 0])
+    hin = synth.host_inputs(w, seed=12)
+    p, x = f64_params(hin), hin.x.astype(np.float64)
+    xa, xb = x[:P], x[P:]
+    empty = [[(np.zeros((0, H)), np.zeros((0, H)))] for _ in range(layers)]
+    y_full, app_full = om.selective_iteration(p, [om.Req(0, P, 0)], xa, empty, 4, 1e-5)
+    y_b, _ = om.selective_iteration(p, [om.Req(0, 5, 0)], xb, empty, 4, 1e-5)
+    bounds = [0, *cuts, P]
+    cache = empty
+    ys = []
+    for c0, c1 in zip(bounds[:-1], bounds[1:]):
+        # the chunk shares the batch with request b's initiation
+        reqs = [om.Req(0, c1 - c0, c0), om.Req(c1 - c0, 5, 0)]
+        caches = [[cache[l][0], (np.zeros((0, H)), np.zeros((0, H)))] for l in range(layers)]
+        y, app = om.selective_iteration(p, reqs, np.concatenate([xa[c0:c1], xb]), caches, 4,
+                                        1e-5)
+        ys.append(y[:c1 - c0])
+        assert rel_err(y[c1 - c0:], y_b) < 1e-12
+        cache = [[(np.concatenate([cache[l][0][0], app[l][0][0]]),
+                   np.concatenate([cache[l][0][1], app[l][0][1]]))] for l in range(layers)]
+    assert rel_err(np.concatenate(ys), y_full) < 1e-12
+    for l in range(layers):
+        assert rel_err(cache[l][0][0], app_full[l][0][0]) < 1e-12
+        assert rel_err(cache[l][0][1], app_full[l][0][1]) < 1e-12
+
+
 # ----------------------------------------------------------- shape pins
 
 def test_shape_pins_of_the_figure():

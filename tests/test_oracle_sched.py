@@ -224,3 +224,130 @@ def test_double_free_raises():
     a.free(b)
     with pytest.raises(KeyError):
         a.free(b)
+
+
+# ------------------------------------------------ cancel and chunked prefill
+
+Scheduler, INITIATION, INCREMENT = osch.Scheduler, osch.INITIATION, osch.INCREMENT
+
+def _steps(s, now=0.0, limit=1000):
+    out = []
+    for _ in range(limit):
+        b = s.step(now)
+        if not b:
+            if s.idle():
+                return out
+            now = s.next_arrival()
+            continue
+        out.append([(e.id, e.q_offset, e.q_len, e.kv_len, e.phase) for e in b])
+        now += 1.0
+    raise AssertionError("did not drain")
+
+
+def test_chunked_hand_example():
+    # budget 4: A's 6-token prompt goes 4 + 2, B's 3-token prompt 2 + 1; A's
+    # first token comes with its last chunk, then it decodes; worked by hand
+    # from the policy (increments, continuing chunks, admissions)
+    s = Scheduler(max_batch=4, token_budget=4, kv_slots=100, policy="chunked")
+    assert s.submit(0, 0.0, 6, 2, 2) and s.submit(1, 0.0, 3, 1, 1)
+    got = _steps(s)
+    I, D = INITIATION, INCREMENT
+    assert got == [
+        [(0, 0, 4, 0, I)],
+        [(0, 0, 2, 4, I), (1, 2, 2, 0, I)],
+        [(0, 0, 1, 6, D), (1, 1, 1, 2, I)],
+    ]
+    a, b = s.requests[0], s.requests[1]
+    assert (a.admitted_at, a.finished_at, a.released_at) == (0, 2, 3)
+    assert (b.admitted_at, b.finished_at, b.released_at) == (1, 2, 3)
+    assert s.used == 0 and s.alloc.used() == 0
+
+
+def test_chunked_equals_iteration_when_budget_never_binds():
+    rng = np.random.default_rng(5)
+    reqs = []
+    for i in range(40):
+        mt = int(rng.integers(1, 20))
+        reqs.append((i, float(rng.uniform(0, 30)), int(rng.integers(1, 50)), mt,
+                     int(rng.integers(1, mt + 1))))
+    logs = []
+    for pol in ("iteration", "chunked"):
+        s = Scheduler(max_batch=5, token_budget=10**6, kv_slots=10**6, policy=pol)
+        for r in reqs:
+            assert s.submit(*r)
+        logs.append(_steps(s))
+    assert logs[0] == logs[1]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_chunked_invariants(seed):
+    rng = np.random.default_rng(40 + seed)
+    budget = int(rng.integers(3, 30))
+    s = Scheduler(max_batch=int(rng.integers(1, 8)), token_budget=budget, kv_slots=2000,
+                  policy="chunked")
+    reqs = {}
+    for i in range(50):
+        mt = int(rng.integers(1, 20))
+        r = (i, float(rng.uniform(0, 40)), int(rng.integers(1, 80)), mt,
+             int(rng.integers(1, mt + 1)))
+        assert s.submit(*r)
+        reqs[i] = r
+    prompt_rows = {i: 0 for i in reqs}
+    incr = {i: 0 for i in reqs}
+    for batch in _steps(s):
+        assert sum(q for _, _, q, _, _ in batch) <= budget
+        phases = [ph for *_, ph in batch]
+        assert phases == sorted(phases, reverse=True)      # increments first
+        off = 0
+        for rid, q_off, q, kv, ph in batch:
+            assert q_off == off
+            off += q
+            if ph == INITIATION:
+                assert kv == prompt_rows[rid]                  # chunks follow each other
+                prompt_rows[rid] += q
+            else:
+                assert q == 1 and prompt_rows[rid] == reqs[rid][2]
+                assert kv == reqs[rid][2] + incr[rid]
+                incr[rid] += 1
+    for i, (_, _, prompt, _, out) in reqs.items():
+        assert prompt_rows[i] == prompt and incr[i] == out - 1
+
+
+def test_cancel_hand_example():
+    # 20 slots: A reserves 15, B (10) must wait; cancelling A frees its slots
+    # at the next step, where B is admitted in its place
+    s = Scheduler(max_batch=2, token_budget=100, kv_slots=20, policy="iteration")
+    assert s.submit(0, 0.0, 5, 10, 10) and s.submit(1, 0.0, 3, 7, 2)
+    assert s.submit(2, 50.0, 2, 2, 1)
+    assert [e.id for e in s.step(0.0)] == [0]
+    assert s.cancel(0)
+    assert not s.cancel(0)                     # twice
+    assert not s.cancel(7)                     # unknown
+    assert s.cancel(2)                         # not arrived yet: dropped at once
+    b = s.step(1.0)
+    assert [(e.id, e.phase, e.kv_base) for e in b] == [(1, INITIATION, 0)]
+    assert [(e.id, e.phase, e.kv_len) for e in s.step(2.0)] == [(1, INCREMENT, 3)]
+    assert s.step(3.0) == [] and s.idle()
+    a, bb, c = s.requests[0], s.requests[1], s.requests[2]
+    assert (a.admitted_at, a.finished_at, a.released_at) == (0, -1, 1)
+    assert (bb.admitted_at, bb.finished_at, bb.released_at) == (1, 2, 3)
+    assert (c.admitted_at, c.released_at) == (-1, -1)
+    assert not s.cancel(1)                     # already released
+    assert s.used == 0
+
+
+def test_cancel_static_leaves_the_rest_of_the_batch_running():
+    s = Scheduler(max_batch=3, token_budget=100, kv_slots=100, policy="static")
+    for i, out in enumerate([5, 5, 5]):
+        assert s.submit(i, 0.0, 2, 5, out)
+    assert s.submit(3, 0.0, 2, 5, 1)
+    assert [e.id for e in s.step(0.0)] == [0, 1, 2]
+    assert s.cancel(1)
+    b = s.step(1.0)
+    assert [e.id for e in b] == [0, 2]          # the cancelled member left at once
+    assert s.requests[1].released_at == 1 and s.used == 14
+    while True:
+        b = s.step(2.0)
+        if not b or 3 in [e.id for e in b]:
+            break
+    assert [e.id for e in b] == [3]             # next batch only after 0 and 2 end
