@@ -74,19 +74,32 @@ class TraceEngine:
         self.y = torch.empty_like(self.x)
 
     def run(self, requests: List[synth.TraceRequest], max_batch: int, token_budget: int,
-            policy: int, log=None, max_wall: float = 1e9) -> dict:
+            policy: int, log=None, max_wall: float = 1e9, depth: int = 1) -> dict:
+        """Serve `requests` under `policy`.  depth = iterations the loop keeps
+        queued on the stream: 1 waits for every iteration before the next
+        scheduling step; 2 or more schedule and launch iteration k+1 while k
+        still runs, so the host's step, validation and launches hide behind
+        the GPU ([0h-n0] implementation notes: the controller does not wait
+        on the engine between batches).  The step clock is the host clock
+        either way; an iteration's end time is read from a timing event."""
         import torch
+        from collections import deque
         log = log or (lambda *a: None)
+        assert 1 <= depth <= 4, "the engine's metadata ring holds 4 batches in flight"
         s = L.orca_sched_create(self.kv, max_batch, token_budget, policy)
         stream = torch.cuda.current_stream()
         try:
             for r in requests:
                 L.orca_sched_submit(s, r.id, r.arrival, r.prompt_len, r.max_tokens, r.out_len)
             torch.cuda.synchronize()
+            start = torch.cuda.Event(enable_timing=True)
+            start.record(stream)
             t0 = time.perf_counter()
             now = 0.0
             steps: List[tuple] = []      # non-empty iterations: (now, ids)
             calls: List[tuple] = []      # every scheduling step, for replay
+            ends: List = []              # timing event after each iteration
+            flight = deque()
             iters = rows = busy = 0
             last_print = t0
             while not L.orca_sched_idle(s):
@@ -99,39 +112,48 @@ class TraceEngine:
                     if nxt is None:
                         raise RuntimeError("scheduler idle with active requests")
                     # nothing to run until the next arrival: wait for it
+                    stream.synchronize()
+                    flight.clear()
                     time.sleep(max(0.0, nxt - (time.perf_counter() - t0)))
                     now = max(time.perf_counter() - t0, nxt)
                     continue
                 n_rows = descs[-1].q_offset + descs[-1].q_len
                 L.orca_iteration(self.ctx, descs, self.x, self.y, self.ws, self.ws_bytes, stream)
-                stream.synchronize()
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record(stream)
+                ends.append(ev)
+                flight.append(ev)
                 steps.append((now, tuple(ids)))
                 iters += 1
                 rows += n_rows
                 busy += len(descs)
+                # keep at most depth - 1 iterations queued behind the next step
+                while len(flight) >= depth:
+                    flight.popleft().synchronize()
                 now = time.perf_counter() - t0
                 if now > max_wall:
                     raise RuntimeError(f"trace exceeded {max_wall} s")
                 if time.perf_counter() - last_print > 20:
                     log(f"  t={now:.1f}s iterations={iters} rows={rows}")
                     last_print = time.perf_counter()
+            stream.synchronize()
             wall = time.perf_counter() - t0
             # per-request latency: time the iteration holding its last token ended
-            iter_end = [steps[k + 1][0] if k + 1 < len(steps) else wall for k in range(len(steps))]
+            iter_end = [start.elapsed_time(e) * 1e-3 for e in ends]
             lats = []
             for r in requests:
-                adm, fin, _ = L.orca_sched_request_info(s, r.id)
+                _, fin, rel = L.orca_sched_request_info(s, r.id)
                 if policy == L.ORCA_POLICY_STATIC:
-                    # request-level: the response leaves with the whole batch
-                    rel = L.orca_sched_request_info(s, r.id)[2]
-                    t_end = steps[rel][0] if rel < len(steps) else wall
+                    # request-level: the response leaves with the whole batch,
+                    # after the iteration before the step that released it
+                    t_end = iter_end[rel - 1] if 0 < rel <= len(iter_end) else wall
                 else:
                     t_end = iter_end[fin]
                 lats.append(t_end - r.arrival)
             gen = sum(r.out_len for r in requests)
             lats = np.array(lats)
             return {
-                "policy": POLICY_NAMES[policy],
+                "policy": POLICY_NAMES[policy], "depth": depth,
                 "wall_s": round(wall, 3), "iterations": iters, "rows_processed": rows,
                 "generated_tokens": gen,
                 "generated_tokens_per_s": round(gen / wall, 1),
@@ -168,6 +190,8 @@ def main(argv=None):
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--log", default=None, help="write the per-step (now, ids) log as JSON")
     p.add_argument("--max-wall", type=float, default=600.0)
+    p.add_argument("--depth", type=int, default=1,
+                   help="iterations kept queued on the stream (2+: schedule ahead)")
     a = p.parse_args(argv)
     import torch
     log = lambda *m: print(*m, file=sys.stderr, flush=True)
@@ -176,7 +200,7 @@ def main(argv=None):
     eng = TraceEngine(work, a.max_batch, a.token_budget, seed=a.seed, log=log)
     out = {"workload": a.workload, "requests": a.requests, "rate": a.rate,
            "max_batch": a.max_batch, "token_budget": a.token_budget, "kv_slots": eng.cap,
-           "runs": []}
+           "depth": a.depth, "runs": []}
     try:
         # warm the kernels once
         warm = [synth.TraceRequest(10**9, 0.0, 64, 8, 2)]
@@ -187,7 +211,8 @@ def main(argv=None):
                 "chunked": [L.ORCA_POLICY_CHUNKED]}[a.policy]
         for pol in pols:
             log(f"policy {POLICY_NAMES[pol]}: {a.requests} requests at {a.rate}/s")
-            res = eng.run(reqs, a.max_batch, a.token_budget, pol, log=log, max_wall=a.max_wall)
+            res = eng.run(reqs, a.max_batch, a.token_budget, pol, log=log, max_wall=a.max_wall,
+                          depth=a.depth)
             res.pop("steps")
             calls = res.pop("calls")
             log(json.dumps(res))
