@@ -46,6 +46,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", choices=["iteration", "gemm", "decode", "copy"], default=None,
                    help="run one timed region only (for profiling)")
+    p.add_argument("--summarize-traffic", metavar="DIR", default=None,
+                   help="no GPU: turn the rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR "
+                        "(pmc_{gemm,decode,copy}_{FETCH_SIZE,WRITE_SIZE}/run_counter_collection"
+                        ".csv) into profiles/hbm_traffic_<workload>.json")
     return p.parse_args()
 
 
@@ -93,9 +97,59 @@ def measured_traffic(workload, key, files):
             "kernel": rec["kernel"]}
 
 
-def cpu_baseline(model, work, x_dev, layers_total):
-    """The CPU oracle on layer 0 of the same batch (all rows, all requests),
-    fp32 numpy on the host; tokens/s extrapolated to the model's depth."""
+# kernels each timed region launches, as rocprofv3 names them
+TRAFFIC_KERNELS = {"gemm": ("gemm_bf16", "gemm_f32", "skinny_reduce"),
+                   "decode": ("attn_split", "attn_combine"), "copy": ("copyBuffer",)}
+
+
+def _counter_means(path, prefixes):
+    """Mean counter value (KiB) per dispatch of every kernel whose name holds
+    one of `prefixes`, keyed by the kernel's short name."""
+    import csv
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if not any(p in name for p in prefixes):
+                continue
+            short = name.split("(")[0].replace("void ", "")
+            vals.setdefault(short, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def summarize_traffic(src, workload):
+    """HBM bytes per launch of the FFN1 GEMM and the decode attention from
+    the counter runs, each counter scaled by what it reads for a plain copy
+    of 1 GiB read + 1 GiB written (bench.py --only copy)."""
+    def run(what, counter):
+        return _counter_means(os.path.join(src, f"pmc_{what}_{counter}",
+                                           "run_counter_collection.csv"), TRAFFIC_KERNELS[what])
+    gib_kib = float(1 << 20)
+    copy_f = max(run("copy", "FETCH_SIZE").values())
+    copy_w = max(run("copy", "WRITE_SIZE").values())
+    fs, ws = gib_kib / copy_f, gib_kib / copy_w
+    out = {"workload": workload, "fetch_scale": fs, "write_scale": ws}
+    for key, what, files in (("gemm_ffn1", "gemm", ["gemm.hip", "device.h", "kernels.h"]),
+                             ("decode", "decode", ["attn.hip", "device.h", "kernels.h"])):
+        f, w = run(what, "FETCH_SIZE"), run(what, "WRITE_SIZE")
+        if not f:
+            continue
+        out[key] = {"kernel": " + ".join(sorted(f)), "source_hash": source_hash(files),
+                    "fetch_kib": {k: round(v, 1) for k, v in f.items()},
+                    "write_kib": {k: round(v, 1) for k, v in w.items()},
+                    "fetch_bytes": sum(f.values()) * 1024 * fs,
+                    "write_bytes": sum(w.values()) * 1024 * ws}
+    dst = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    with open(dst, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def cpu_baseline(model, work, x_dev, layers_total, min_seconds=10.0):
+    """The CPU oracle on the same batch (all rows, all requests), fp32 numpy
+    on the host: layers 0, 1, ... in order (each layer's output feeds the
+    next) until at least `min_seconds` of work or every layer is done;
+    tokens/s extrapolated to the model's depth."""
     import numpy as np
     from oracle import model as om
     try:
@@ -103,24 +157,32 @@ def cpu_baseline(model, work, x_dev, layers_total):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count()
-    p = {k: v.float().cpu().numpy() for k, v in model.weights[0].items()}
     x = x_dev.float().cpu().numpy()
-    caches = [[model.cache_rows(0, i, 0, work.kv_len[i]) for i in range(work.n_reqs)]]
     reqs, off = [], 0
     for q, kv in zip(work.q_len, work.kv_len):
         reqs.append(om.Req(off, q, kv))
         off += q
-    t0 = time.perf_counter()
-    om.selective_layer(p, reqs, x, caches[0], work.heads, work.eps)
-    dt = time.perf_counter() - t0
-    return {"value": work.rows / (dt * layers_total), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"layer 0 of {layers_total} ({work.rows} rows, {work.n_reqs} requests), "
-                      f"numpy fp32, {dt:.1f} s; extrapolated x{layers_total} layers"}
+    spent, done = 0.0, 0
+    while done < layers_total and spent < min_seconds:
+        p = {k: v.float().cpu().numpy() for k, v in model.weights[done].items()}
+        caches = [model.cache_rows(done, i, 0, work.kv_len[i]) for i in range(work.n_reqs)]
+        t0 = time.perf_counter()
+        x = om.selective_layer(p, reqs, x, caches, work.heads, work.eps)[0]
+        spent += time.perf_counter() - t0
+        done += 1
+    per_layer = spent / done
+    return {"value": work.rows / (per_layer * layers_total), "unit": "tokens/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"layers 0-{done - 1} of {layers_total} ({work.rows} rows, {work.n_reqs} "
+                      f"requests), numpy fp32, {spent:.1f} s; extrapolated to {layers_total} "
+                      f"layers"}
 
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the iteration has no multi-GPU path in this build)", file=sys.stderr)
@@ -187,16 +249,39 @@ def main():
         for _ in range(3):
             ffn1()
         gms = time_events(ffn1, args.kernel_reps, stream)
-        tflops = 2.0 * M * F * H / (gms * 1e-3) / 1e12
+        flops = 2.0 * M * F * H
+        esz = 2 if bf16 else 4
+        # algorithmic bytes: W, A and the output once each
+        alg_bytes = esz * (F * H + M * H + M * F)
         peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+        ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)            # FLOP per byte
+        split = gws_bytes > 0
         tr = measured_traffic(work.name, "gemm_ffn1", ["gemm.hip", "device.h", "kernels.h"])
-        gemm = {"bound": "mfma", "kernel": (tr["kernel"] if tr else "gemm_bf16_kernel<gelu>") +
-                " (FFN1)" if bf16 else "gemm_f32_kernel<gelu> (FFN1)", "shape": [M, F, H],
-                "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(tflops / peak, 4), "traffic": tr["bytes"] if tr else None,
-                "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
-                "algorithmic_flops": 2 * M * F * H, "ms_per_launch": round(gms, 4)}
-        log(f"FFN1 GEMM {M}x{F}x{H}: {gms:.3f} ms, {tflops:.1f} TFLOP/s")
+        if tr:
+            kname = tr["kernel"]
+        elif bf16:
+            kname = "gemm_bf16_kernel<gelu>" + (" split-K + skinny_reduce_kernel<gelu>"
+                                                 if split else "")
+        else:
+            kname = "gemm_f32_kernel<gelu>"
+        common = {"kernel": kname + " (FFN1)", "shape": [M, F, H],
+                  "traffic": tr["bytes"] if tr else None,
+                  "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
+                  "algorithmic_flops": int(flops), "algorithmic_bytes": int(alg_bytes),
+                  "arithmetic_intensity": round(flops / alg_bytes, 1),
+                  "ms_per_launch": round(gms, 4)}
+        tflops = flops / (gms * 1e-3) / 1e12
+        if flops / alg_bytes >= ridge:
+            gemm = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(tflops / peak, 4), **common}
+        else:
+            # few rows: the weights stream once and the MFMAs idle
+            gbs = alg_bytes / (gms * 1e-3) / 1e9
+            gemm = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "achieved_tflops": round(tflops, 2), **common}
+        log(f"FFN1 GEMM {M}x{F}x{H}: {gms:.3f} ms, {tflops:.1f} TFLOP/s, "
+            f"{alg_bytes / (gms * 1e-3) / 1e9:.0f} GB/s algorithmic")
         del a, f
 
     decode = None
