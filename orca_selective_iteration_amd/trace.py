@@ -79,9 +79,12 @@ class TraceEngine:
         queued on the stream: 1 waits for every iteration before the next
         scheduling step; 2 or more schedule and launch iteration k+1 while k
         still runs, so the host's step, validation and launches hide behind
-        the GPU ([0h-n0] implementation notes: the controller does not wait
-        on the engine between batches).  The step clock is the host clock
-        either way; an iteration's end time is read from a timing event."""
+        the GPU (garden.houmin.site/infra/orca 3.1.3: the scheduler keeps up
+        to n_workers batches in the engine without waiting for one to
+        return; unpurerationalist.github.io ORCA notes 4.1: a controller
+        hands its kernels to the GPU and goes on without waiting).  The step
+        clock is the host clock either way; an iteration's end time is read
+        from a timing event."""
         import torch
         from collections import deque
         log = log or (lambda *a: None)
