@@ -112,6 +112,20 @@ def test_linear(dtype, m, n, k, epi, workspace):
     assert rel_err(got, ref) < TOL[dtype]
 
 
+@pytest.mark.parametrize("variant", ["0", "3", "6", "7", "10"])
+@pytest.mark.parametrize("m,n,k,epi", [
+    (300, 1024, 1024, L.ORCA_EPI_BIAS_GELU), (520, 768, 2048, L.ORCA_EPI_BIAS_RESID),
+    (64, 1536, 512, L.ORCA_EPI_BIAS), (33, 640, 2048, L.ORCA_EPI_BIAS_GELU)])
+def test_linear_every_variant(variant, m, n, k, epi, monkeypatch):
+    """Each tile variant (pinned), and the split-K path, against the oracle."""
+    print(f"case linear variant {variant} m={m} n={n} k={k} epi={epi}", flush=True)
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", variant)
+    got, ref, nb = _linear_case("bf16", m, n, k, epi, True)
+    if variant == "10":
+        assert nb > 0
+    assert rel_err(got, ref) < TOL["bf16"]
+
+
 def test_linear_empty_batch_is_noop():
     out = torch.full((4, 128), 3.0, device=DEV)
     a = torch.zeros((4, 64), device=DEV, dtype=torch.bfloat16)
@@ -121,11 +135,15 @@ def test_linear_empty_batch_is_noop():
 
 # ------------------------------------------------------------- QKV + append
 
-@pytest.mark.parametrize("dtype,m,hidden,heads", [
-    ("bf16", 7, 256, 2), ("bf16", 133, 512, 8), ("bf16", 64, 1024, 8), ("f32", 7, 64, 4),
-    ("f32", 70, 256, 8)])
-def test_qkv_split_and_append(dtype, m, hidden, heads):
-    print(f"case qkv {dtype} m={m} hidden={hidden} heads={heads}", flush=True)
+@pytest.mark.parametrize("dtype,m,hidden,heads,variant", [
+    ("bf16", 7, 256, 2, None), ("bf16", 133, 512, 8, None), ("bf16", 64, 1024, 8, None),
+    ("f32", 7, 64, 4, None), ("f32", 70, 256, 8, None),
+    ("bf16", 300, 512, 4, "6"), ("bf16", 300, 512, 4, "0"), ("bf16", 300, 512, 4, "10"),
+    ("bf16", 40, 1024, 8, "10")])
+def test_qkv_split_and_append(dtype, m, hidden, heads, variant, monkeypatch):
+    if variant is not None:
+        monkeypatch.setenv("ORCA_GEMM_VARIANT", variant)
+    print(f"case qkv {dtype} m={m} hidden={hidden} heads={heads} variant={variant}", flush=True)
     rng = np.random.default_rng(m + hidden)
     d = hidden // heads
     cap = 3 * m + 5
