@@ -410,13 +410,16 @@ static void launch_mfma(const void* a, const void* w, const void* bias, const Ep
 // fill the GPU (k % 64 == 0, n % 4 == 0).  Tile by rows: 32 x 128 or
 // 64 x 128 (four waves side by side along N) up to 64 rows, else 128 x 128.
 // grid.y splits the K steps, an even count per split (the two-step
-// pipeline), so the grid holds about SPLIT_TARGET_WG workgroups; the fp32
-// partial buffer is then bounded by about SPLIT_TARGET_WG tile areas.
+// pipeline).  The split count is rounded down so the grid fits in one round
+// of resident workgroups (two per CU): every workgroup streams the same
+// share of K, and a second, mostly idle round would cost as much as the
+// first.
 struct SplitPlan {
   int tile;   // 0: 32 x 128, 1: 64 x 128, 2: 128 x 128
   int tiles, kt_per_split, splits;
 };
-constexpr int SPLIT_TARGET_WG = 512;
+constexpr int NUM_CU = 256;              // MI355X
+constexpr int LDS_PER_CU = 160 * 1024;
 static int env_int(const char* name, int dflt) {
   const char* f = getenv(name);
   return f ? atoi(f) : dflt;
@@ -426,11 +429,14 @@ static bool split_plan(int m, int n, int k, SplitPlan& p) {
   p.tile = m <= 32 ? 0 : m <= 64 ? 1 : 2;
   const int bm = p.tile == 0 ? 32 : p.tile == 1 ? 64 : 128;
   p.tiles = ((m + bm - 1) / bm) * ((n + 127) / 128);
-  const int target = std::max(1, env_int("ORCA_SPLIT_TARGET", SPLIT_TARGET_WG));
+  // resident workgroups: the double-buffered A and W stages bound them by
+  // LDS; more than two per CU measured no faster (their loads compete)
+  const int lds = 2 * (bm + 128) * LDK * 2;
+  const int resident = NUM_CU * std::max(1, std::min(2, LDS_PER_CU / lds));
+  const int target = std::max(1, env_int("ORCA_SPLIT_TARGET", resident));
   if (2 * p.tiles > target) return false;   // enough tiles already
   const int kt = k / BK;
-  const int splits = std::max(1, std::min({(target + p.tiles - 1) / p.tiles, SPLIT_MAX_SPLITS,
-                                           std::max(1, kt / 4)}));
+  const int splits = std::max(1, std::min({target / p.tiles, SPLIT_MAX_SPLITS, std::max(1, kt / 4)}));
   int per = (kt + splits - 1) / splits;
   if (kt % 2 == 0) per += per & 1;
   p.kt_per_split = per;
