@@ -304,7 +304,7 @@ orca_status orca_create(const orca_model_desc* desc, const orca_layer_weights* l
   c->off_part_ml = take(size_t(c->max_items) * d.heads * 2 * 4);
   // split-K partial sums of the Linear layers: the largest need over every
   // row count the context accepts
-  for (int m = 1; m <= std::min<int>(max_rows, SPLIT_MAX_M); ++m) {
+  for (int m = 1; m <= max_rows; ++m) {
     const int hh = d.hidden, ff = d.ffn;
     c->gpart_bytes = std::max({c->gpart_bytes, linear_workspace_bytes(d.dtype, m, 3 * hh, hh),
                                linear_workspace_bytes(d.dtype, m, hh, hh),

@@ -377,9 +377,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 //   3: 4x2 waves, 2x4 tiles -> 256 x 256, 512 threads
 //   6: as 3, with two K steps of global loads in flight (default, large)
 //   7: as 0, with two K steps of global loads in flight (default, small)
-//  10: split-K (default when the tiles are too few to fill the GPU, the
-//      rows are at most SPLIT_MAX_M and the caller passes a large enough
-//      workspace; else variant 7)
+//  10: split-K (default when the tiles are too few to fill the GPU and the
+//      caller passes a large enough workspace; see split_plan)
 // (6 and 7 need an even number of K steps and fall back to 3 and 0.)
 // ORCA_GEMM_VARIANT=<n> pins the variant (tests and tuning runs).
 static int choose_variant(int m, int n) {
@@ -387,12 +386,7 @@ static int choose_variant(int m, int n) {
     const int v = atoi(f);
     if (v == 0 || v == 3 || v == 6 || v == 7 || v == 10) return v;
   }
-  // measured on MI355X at the 13B / 175B layer shapes: the 8-wave 256 x 256
-  // tile with two K steps in flight (variant 6) is fastest once it yields
-  // enough tiles to spread over the 256 CUs; below that the 128 x 128 tile
-  // (variant 7) keeps more CUs busy
-  const long big = (long)((m + 255) / 256) * ((n + 255) / 256);
-  return big >= 128 ? 6 : -1;
+  return -1;   // automatic: split-K where it applies, else by tile count
 }
 
 template <int EPI, int WGM, int WGN, int TI, int TJ, bool PIPE = false>
@@ -415,7 +409,7 @@ static void launch_mfma(const void* a, const void* w, const void* bias, const Ep
 // share of K, and a second, mostly idle round would cost as much as the
 // first.
 struct SplitPlan {
-  int tile;   // 0: 32 x 128, 1: 64 x 128, 2: 128 x 128
+  int tile;   // 0: 32 x 128, 1: 64 x 128, 2: 128 x 128, 3: 256 x 256
   int tiles, kt_per_split, splits;
 };
 constexpr int NUM_CU = 256;              // MI355X
@@ -424,23 +418,52 @@ static int env_int(const char* name, int dflt) {
   const char* f = getenv(name);
   return f ? atoi(f) : dflt;
 }
-static bool split_plan(int m, int n, int k, SplitPlan& p) {
-  if (m < 1 || m > env_int("ORCA_SPLIT_MAX_M", SPLIT_MAX_M) || k % BK || n % 4) return false;
-  p.tile = m <= 32 ? 0 : m <= 64 ? 1 : 2;
-  const int bm = p.tile == 0 ? 32 : p.tile == 1 ? 64 : 128;
-  p.tiles = ((m + bm - 1) / bm) * ((n + 127) / 128);
-  // resident workgroups: the double-buffered A and W stages bound them by
-  // LDS; more than two per CU measured no faster (their loads compete)
-  const int lds = 2 * (bm + 128) * LDK * 2;
-  const int resident = NUM_CU * std::max(1, std::min(2, LDS_PER_CU / lds));
-  const int target = std::max(1, env_int("ORCA_SPLIT_TARGET", resident));
-  if (2 * p.tiles > target) return false;   // enough tiles already
-  const int kt = k / BK;
-  const int splits = std::max(1, std::min({target / p.tiles, SPLIT_MAX_SPLITS, std::max(1, kt / 4)}));
+static void set_splits(int kt, int splits, SplitPlan& p) {
   int per = (kt + splits - 1) / splits;
-  if (kt % 2 == 0) per += per & 1;
+  if (kt % 2 == 0) per += per & 1;   // even K steps per split: the two-step pipeline
   p.kt_per_split = per;
   p.splits = (kt + per - 1) / per;
+}
+// Fraction of the resident slots the launch keeps busy over its rounds.
+static double round_fill(long units, long slots) {
+  return (double)units / (double)(((units + slots - 1) / slots) * slots);
+}
+static bool split_plan(int m, int n, int k, SplitPlan& p) {
+  if (m < 1 || k % BK || n % 4) return false;
+  const int kt = k / BK;
+  if (m <= env_int("ORCA_SPLIT_MAX_M", SPLIT_MAX_M)) {
+    p.tile = m <= 32 ? 0 : m <= 64 ? 1 : 2;
+    const int bm = p.tile == 0 ? 32 : p.tile == 1 ? 64 : 128;
+    p.tiles = ((m + bm - 1) / bm) * ((n + 127) / 128);
+    // resident workgroups: the double-buffered A and W stages bound them by
+    // LDS; more than two per CU measured no faster (their loads compete)
+    const int lds = 2 * (bm + 128) * LDK * 2;
+    const int resident = NUM_CU * std::max(1, std::min(2, LDS_PER_CU / lds));
+    const int target = std::max(1, env_int("ORCA_SPLIT_TARGET", resident));
+    if (2 * p.tiles <= target) {
+      set_splits(kt, std::max(1, std::min({target / p.tiles, SPLIT_MAX_SPLITS, std::max(1, kt / 4)})), p);
+      return p.splits > 1;
+    }
+  }
+  // 256 x 256 tiles (one resident per CU) that leave part of the only round
+  // idle: split K by 2-4 when whole rounds then fill markedly better and
+  // every split keeps at least 40 K steps (the partial sums are read back
+  // once; with less K per split they cost more than the idle CUs)
+  p.tile = 3;
+  p.tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  if (p.tiles < 128 || p.tiles >= NUM_CU || kt % 2) return false;
+  int best = 1;
+  double fill = round_fill(p.tiles, NUM_CU);
+  for (int sp = 2; sp <= 4; ++sp) {
+    if (kt / sp < 40) break;
+    const double f = round_fill((long)p.tiles * sp, NUM_CU);
+    if (f > fill + 0.1) {
+      best = sp;
+      fill = f;
+    }
+  }
+  if (best == 1) return false;
+  set_splits(kt, best, p);
   return p.splits > 1;
 }
 
@@ -469,7 +492,8 @@ static void launch_split(const SplitPlan& p, const void* a, const void* w, const
   pp.ldo = n;
   if (p.tile == 0) launch_partial<1, 4, 1, 1>(p, a, w, pp, m, n, k, s);
   else if (p.tile == 1) launch_partial<1, 4, 2, 1>(p, a, w, pp, m, n, k, s);
-  else launch_partial<2, 2, 2, 2>(p, a, w, pp, m, n, k, s);
+  else if (p.tile == 2) launch_partial<2, 2, 2, 2>(p, a, w, pp, m, n, k, s);
+  else launch_partial<4, 2, 2, 4>(p, a, w, pp, m, n, k, s);
   const int threads = m * (n / 4);
   hipLaunchKernelGGL(skinny_reduce_kernel<EPI>, dim3((threads + 255) / 256), dim3(256), 0, s,
                      part, p.splits, (const bf16*)bias, ep, m, n);
@@ -481,11 +505,19 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
                          hipStream_t s) {
   if (dtype == ORCA_BF16) {
     SplitPlan sp;
-    const int v = choose_variant(m, n);
+    int v = choose_variant(m, n);
     if ((v == 10 || v < 0) && ws && split_plan(m, n, k, sp) &&
         ws_bytes >= (size_t)sp.splits * m * n * sizeof(float)) {
       launch_split<EPI>(sp, a, w, bias, ep, static_cast<float*>(ws), m, n, k, s);
       return;
+    }
+    if (v < 0) {
+      // measured on MI355X at the 13B / 175B layer shapes: the 8-wave
+      // 256 x 256 tile with two K steps in flight (variant 6) is fastest once
+      // it yields enough tiles to spread over the 256 CUs; below that the
+      // 128 x 128 tile (variant 7) keeps more CUs busy
+      const long big = (long)((m + 255) / 256) * ((n + 255) / 256);
+      v = big >= 128 ? 6 : 7;
     }
     switch (v) {
       case 0: launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;

@@ -27,8 +27,9 @@ struct QkvDest {
 constexpr int EPI_QKV = 3;
 // internal: fp32 partial sums of a K split, no bias (the few-rows path)
 constexpr int EPI_PARTIAL = 4;
-// bf16 problems of at most SPLIT_MAX_M rows whose tiles are too few to fill
-// the GPU take a split-K path when `ws` holds
+// bf16 problems whose tiles are too few to fill the GPU (up to SPLIT_MAX_M
+// rows on 32/64/128-row tiles; 256 x 256 tiles short of one round when
+// splitting K fills whole rounds better) take a split-K path when `ws` holds
 // linear_workspace_bytes(dtype, m, n, k) bytes (fp32 partial sums);
 // otherwise, and for every other shape, the tiled kernels run and `ws` is
 // not touched.
