@@ -512,12 +512,14 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
       return;
     }
     if (v < 0) {
-      // measured on MI355X at the 13B / 175B layer shapes: the 8-wave
-      // 256 x 256 tile with two K steps in flight (variant 6) is fastest once
-      // it yields enough tiles to spread over the 256 CUs; below that the
-      // 128 x 128 tile (variant 7) keeps more CUs busy
+      // The 8-wave 256 x 256 tile (variant 6, one per CU) runs a full round
+      // at ~1.18x the rate of the 128 x 128 tile (variant 7, two per CU),
+      // measured on the 13B FFN1 shape; what decides is how well each fills
+      // its last round (the 13B QKV: 540 big tiles fill 3 rounds to 70%,
+      // 2040 small ones 4 rounds to 99.6%, so variant 7 is faster there).
       const long big = (long)((m + 255) / 256) * ((n + 255) / 256);
-      v = big >= 128 ? 6 : 7;
+      const long small = (long)((m + 127) / 128) * ((n + 127) / 128);
+      v = big >= 128 && round_fill(big, NUM_CU) >= 0.845 * round_fill(small, 2 * NUM_CU) ? 6 : 7;
     }
     switch (v) {
       case 0: launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;
