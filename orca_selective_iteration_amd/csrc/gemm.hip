@@ -372,23 +372,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 // ---------------------------------------------------------------- launcher
 
-// Tile shape for an M x N output.  Variants (wave grid x per-wave tiles):
+// Tile variants (wave grid x per-wave 32x32 tiles):
 //   0: 2x2 waves, 2x2 tiles -> 128 x 128, 256 threads, 2 workgroups / CU
 //   3: 4x2 waves, 2x4 tiles -> 256 x 256, 512 threads
-//   6: as 3, with two K steps of global loads in flight (default, large)
-//   7: as 0, with two K steps of global loads in flight (default, small)
-//  10: split-K (default when the tiles are too few to fill the GPU and the
-//      caller passes a large enough workspace; see split_plan)
-// (6 and 7 need an even number of K steps and fall back to 3 and 0.)
-// ORCA_GEMM_VARIANT=<n> pins the variant (tests and tuning runs).
-static int choose_variant(int m, int n) {
-  if (const char* f = getenv("ORCA_GEMM_VARIANT")) {
-    const int v = atoi(f);
-    if (v == 0 || v == 3 || v == 6 || v == 7 || v == 10) return v;
-  }
-  return -1;   // automatic: split-K where it applies, else by tile count
-}
-
+//   6: as 3, with two K steps of global loads in flight
+//   7: as 0, with two K steps of global loads in flight
+//   8: 4x2 waves, 2x3 tiles -> 256 x 192, 512 threads, two K steps in flight
+//  10: split-K (see plan_gemm)
+// (6, 7 and 8 need an even number of K steps and fall back to 3, 0 and the
+// one-step 256 x 192 form.)
 template <int EPI, int WGM, int WGN, int TI, int TJ, bool PIPE = false>
 static void launch_mfma(const void* a, const void* w, const void* bias, const EpiParams& ep, int m,
                         int n, int k, hipStream_t s, int splits = 1, int kt_per_split = 0) {
@@ -400,14 +392,9 @@ static void launch_mfma(const void* a, const void* w, const void* bias, const Ep
                      kt_per_split > 0 ? kt_per_split : k / BK);
 }
 
-// Split-K plan for an m x n x k bf16 problem whose tiles are too few to
-// fill the GPU (k % 64 == 0, n % 4 == 0).  Tile by rows: 32 x 128 or
-// 64 x 128 (four waves side by side along N) up to 64 rows, else 128 x 128.
-// grid.y splits the K steps, an even count per split (the two-step
-// pipeline).  The split count is rounded down so the grid fits in one round
-// of resident workgroups (two per CU): every workgroup streams the same
-// share of K, and a second, mostly idle round would cost as much as the
-// first.
+// Split-K plan: tile, tile count, K steps per split, splits.  grid.y splits
+// the K steps, an even count per split (the two-step pipeline); each split
+// writes fp32 partial sums that skinny_reduce_kernel adds up.
 struct SplitPlan {
   int tile;   // 0: 32 x 128, 1: 64 x 128, 2: 128 x 128, 3: 256 x 256
   int tiles, kt_per_split, splits;
@@ -420,56 +407,100 @@ static int env_int(const char* name, int dflt) {
 }
 static void set_splits(int kt, int splits, SplitPlan& p) {
   int per = (kt + splits - 1) / splits;
-  if (kt % 2 == 0) per += per & 1;   // even K steps per split: the two-step pipeline
+  if (kt % 2 == 0) per += per & 1;
   p.kt_per_split = per;
   p.splits = (kt + per - 1) / per;
 }
-// Fraction of the resident slots the launch keeps busy over its rounds.
-static double round_fill(long units, long slots) {
-  return (double)units / (double)(((units + slots - 1) / slots) * slots);
-}
-static bool split_plan(int m, int n, int k, SplitPlan& p) {
-  if (m < 1 || k % BK || n % 4) return false;
+static long ceil_div_l(long a, long b) { return (a + b - 1) / b; }
+
+// Few rows (up to SPLIT_MAX_M) whose 32/64/128-row tiles are too few to fill
+// the GPU: split K so the grid fills one round of resident workgroups (two
+// per CU, bounded by LDS; more measured no faster), rounded down: every
+// workgroup streams the same share of K, and a second, mostly idle round
+// would cost as much as the first.
+static bool few_rows_plan(int m, int n, int k, SplitPlan& p) {
+  if (m > env_int("ORCA_SPLIT_MAX_M", SPLIT_MAX_M)) return false;
   const int kt = k / BK;
-  if (m <= env_int("ORCA_SPLIT_MAX_M", SPLIT_MAX_M)) {
-    p.tile = m <= 32 ? 0 : m <= 64 ? 1 : 2;
-    const int bm = p.tile == 0 ? 32 : p.tile == 1 ? 64 : 128;
-    p.tiles = ((m + bm - 1) / bm) * ((n + 127) / 128);
-    // resident workgroups: the double-buffered A and W stages bound them by
-    // LDS; more than two per CU measured no faster (their loads compete)
-    const int lds = 2 * (bm + 128) * LDK * 2;
-    const int resident = NUM_CU * std::max(1, std::min(2, LDS_PER_CU / lds));
-    const int target = std::max(1, env_int("ORCA_SPLIT_TARGET", resident));
-    if (2 * p.tiles <= target) {
-      set_splits(kt, std::max(1, std::min({target / p.tiles, SPLIT_MAX_SPLITS, std::max(1, kt / 4)})), p);
-      return p.splits > 1;
-    }
-  }
-  // 256 x 256 tiles (one resident per CU) that leave part of the only round
-  // idle: split K by 2-4 when whole rounds then fill markedly better and
-  // every split keeps at least 40 K steps (the partial sums are read back
-  // once; with less K per split they cost more than the idle CUs)
-  p.tile = 3;
-  p.tiles = ((m + 255) / 256) * ((n + 255) / 256);
-  if (p.tiles < 128 || p.tiles >= NUM_CU || kt % 2) return false;
-  int best = 1;
-  double fill = round_fill(p.tiles, NUM_CU);
-  for (int sp = 2; sp <= 4; ++sp) {
-    if (kt / sp < 40) break;
-    const double f = round_fill((long)p.tiles * sp, NUM_CU);
-    if (f > fill + 0.1) {
-      best = sp;
-      fill = f;
-    }
-  }
-  if (best == 1) return false;
-  set_splits(kt, best, p);
+  p.tile = m <= 32 ? 0 : m <= 64 ? 1 : 2;
+  const int bm = p.tile == 0 ? 32 : p.tile == 1 ? 64 : 128;
+  p.tiles = ((m + bm - 1) / bm) * ((n + 127) / 128);
+  const int lds = 2 * (bm + 128) * LDK * 2;
+  const int resident = NUM_CU * std::max(1, std::min(2, LDS_PER_CU / lds));
+  const int target = std::max(1, env_int("ORCA_SPLIT_TARGET", resident));
+  if (2 * p.tiles > target) return false;   // enough tiles already
+  set_splits(kt, std::max(1, std::min({target / p.tiles, SPLIT_MAX_SPLITS, std::max(1, kt / 4)})), p);
   return p.splits > 1;
+}
+
+// Estimated time of the tiled launches, in units of one 256 x 256 tile-round
+// per unit of K: rounds of resident workgroups times the output area a CU
+// covers per round, over the tile's measured rate relative to 256 x 256
+// (MI355X, 13B layer shapes, K steps even: 256 x 192 at 0.945, 128 x 128
+// at 0.84).  The last round counts whole: a launch that leaves CUs idle in
+// it pays for them.
+static double cost_tiled(int v, int m, int n) {
+  switch (v) {
+    case 6: return ceil_div_l(ceil_div_l(m, 256) * ceil_div_l(n, 256), NUM_CU) * 65536.0;
+    case 8: return ceil_div_l(ceil_div_l(m, 256) * ceil_div_l(n, 192), NUM_CU) * 49152.0 / 0.945;
+    default: return ceil_div_l(ceil_div_l(m, 128) * ceil_div_l(n, 128), 2 * NUM_CU) * 32768.0 / 0.84;
+  }
+}
+// 256 x 256 tiles with K split by 2-4 (each split at least 40 K steps; its
+// partial sums are written and read back once, charged at 15%).
+static double cost_big_split(int m, int n, int k, SplitPlan& p) {
+  const int kt = k / BK;
+  double best = 1e300;
+  p.tile = 3;
+  p.tiles = (int)(ceil_div_l(m, 256) * ceil_div_l(n, 256));
+  if (kt % 2) return best;
+  for (int sp = 2; sp <= 4 && kt / sp >= 40; ++sp) {
+    const double c = ceil_div_l((long)p.tiles * sp, NUM_CU) * 65536.0 / sp * 1.15;
+    if (c < best) {
+      best = c;
+      set_splits(kt, sp, p);
+    }
+  }
+  return best;
+}
+
+// The launch for one bf16 problem: a tiled variant, or split-K (`split`
+// filled, variant 10).  ORCA_GEMM_VARIANT=<n> pins the variant.
+static int plan_gemm(int m, int n, int k, SplitPlan& split) {
+  int pinned = -1;
+  if (const char* f = getenv("ORCA_GEMM_VARIANT")) {
+    const int v = atoi(f);
+    if (v == 0 || v == 3 || v == 6 || v == 7 || v == 8 || v == 10) pinned = v;
+  }
+  if (pinned >= 0 && pinned != 10) return pinned;
+  if (m >= 1 && k % BK == 0 && n % 4 == 0) {
+    if (few_rows_plan(m, n, k, split)) return 10;
+    // another tile only on a predicted gain of 3% or more over 256 x 256
+    // (the model is coarse; in a full iteration the 175B shapes, where
+    // 256 x 192 was predicted 1% faster, ran 1% slower)
+    int v = 6;
+    double best = cost_tiled(6, m, n) * 0.97;
+    for (int c : {8, 7}) {
+      const double e = cost_tiled(c, m, n);
+      if (e < best) {
+        best = e;
+        v = c;
+      }
+    }
+    SplitPlan bs;
+    if (cost_big_split(m, n, k, bs) < best || pinned == 10) {
+      if (bs.splits > 1 && bs.splits <= SPLIT_MAX_SPLITS) {
+        split = bs;
+        return 10;
+      }
+    }
+    return v;
+  }
+  return 7;
 }
 
 size_t linear_workspace_bytes(int dtype, int m, int n, int k) {
   SplitPlan p;
-  if (dtype != ORCA_BF16 || !split_plan(m, n, k, p)) return 0;
+  if (dtype != ORCA_BF16 || m < 1 || plan_gemm(m, n, k, p) != 10) return 0;
   return (size_t)p.splits * m * n * sizeof(float);
 }
 
@@ -504,22 +535,14 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
                          const EpiParams& ep, void* ws, size_t ws_bytes, int m, int n, int k,
                          hipStream_t s) {
   if (dtype == ORCA_BF16) {
-    SplitPlan sp;
-    int v = choose_variant(m, n);
-    if ((v == 10 || v < 0) && ws && split_plan(m, n, k, sp) &&
-        ws_bytes >= (size_t)sp.splits * m * n * sizeof(float)) {
-      launch_split<EPI>(sp, a, w, bias, ep, static_cast<float*>(ws), m, n, k, s);
-      return;
-    }
-    if (v < 0) {
-      // The 8-wave 256 x 256 tile (variant 6, one per CU) runs a full round
-      // at ~1.18x the rate of the 128 x 128 tile (variant 7, two per CU),
-      // measured on the 13B FFN1 shape; what decides is how well each fills
-      // its last round (the 13B QKV: 540 big tiles fill 3 rounds to 70%,
-      // 2040 small ones 4 rounds to 99.6%, so variant 7 is faster there).
-      const long big = (long)((m + 255) / 256) * ((n + 255) / 256);
-      const long small = (long)((m + 127) / 128) * ((n + 127) / 128);
-      v = big >= 128 && round_fill(big, NUM_CU) >= 0.845 * round_fill(small, 2 * NUM_CU) ? 6 : 7;
+    SplitPlan sp{};
+    int v = plan_gemm(m, n, k, sp);
+    if (v == 10) {
+      if (ws && ws_bytes >= (size_t)sp.splits * m * n * sizeof(float)) {
+        launch_split<EPI>(sp, a, w, bias, ep, static_cast<float*>(ws), m, n, k, s);
+        return;
+      }
+      v = cost_tiled(8, m, n) < cost_tiled(6, m, n) ? 8 : 7;   // no room for the partials
     }
     switch (v) {
       case 0: launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;
@@ -527,6 +550,10 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
       case 6:
         if ((k / BK) % 2 == 0) launch_mfma<EPI, 4, 2, 2, 4, true>(a, w, bias, ep, m, n, k, s);
         else launch_mfma<EPI, 4, 2, 2, 4>(a, w, bias, ep, m, n, k, s);
+        break;
+      case 8:
+        if ((k / BK) % 2 == 0) launch_mfma<EPI, 4, 2, 2, 3, true>(a, w, bias, ep, m, n, k, s);
+        else launch_mfma<EPI, 4, 2, 2, 3>(a, w, bias, ep, m, n, k, s);
         break;
       default:  // 7, and the split-K choice when it does not apply
         if ((k / BK) % 2 == 0) launch_mfma<EPI, 2, 2, 2, 2, true>(a, w, bias, ep, m, n, k, s);
