@@ -236,28 +236,43 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   const bf16* kb = (const bf16*)a.k_pool + head_base;
   const bf16* vb = (const bf16*)a.v_pool + head_base;
 
+  // K and V of the next 64-key step are loaded into registers while the
+  // current step runs on the MFMAs (16-byte loads; keys past the block's
+  // last one re-read it, so the loads never sit behind a branch)
+  constexpr int NL = BKV * (D / 8) / 256;   // 16-byte loads per thread, K and V each
+  static_assert(NL * 256 == BKV * (D / 8) && NL * 4 == D / 8, "tile not divisible by threads");
+  // vector-typed staging (not arrays) keeps the prefetch in registers
+  typedef uint32_t Stage __attribute__((ext_vector_type(4 * NL)));
+  Stage kreg, vreg;
+  const int vkey = tid & 63;
+#define ORCA_PF_LOAD(K0)                                                                     \
+  _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                           \
+    const int c = tid + 256 * i, key = c / (D / 8), ch = c % (D / 8);                        \
+    const uint4 tk = *reinterpret_cast<const uint4*>(                                        \
+        kb + (size_t)min((K0) + key, kend - 1) * D + ch * 8);                                \
+    const uint4 tv = *reinterpret_cast<const uint4*>(                                        \
+        vb + (size_t)min((K0) + vkey, kend - 1) * D + ((tid >> 6) + 4 * i) * 8);             \
+    kreg[4 * i] = tk.x; kreg[4 * i + 1] = tk.y; kreg[4 * i + 2] = tk.z; kreg[4 * i + 3] = tk.w; \
+    vreg[4 * i] = tv.x; vreg[4 * i + 1] = tv.y; vreg[4 * i + 2] = tv.z; vreg[4 * i + 3] = tv.w; \
+  }
+  ORCA_PF_LOAD(0)
   for (int k0 = 0; k0 < kend; k0 += BKV) {
     __syncthreads();
-    for (int c = tid; c < BKV * (D / 8); c += 256) {
-      const int key = c / (D / 8), ch = c % (D / 8);
-      const int kk = min(k0 + key, kend - 1);
-      *reinterpret_cast<uint4*>(&sK[key * KLD + ch * 8]) =
-          *reinterpret_cast<const uint4*>(kb + (size_t)kk * D + ch * 8);
-    }
-    {
-      const int key = tid & 63;
-      const int kk = min(k0 + key, kend - 1);
-      for (int ch = tid >> 6; ch < D / 8; ch += 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(vb + (size_t)kk * D + ch * 8);
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sV[(ch * 8 + 2 * j) * VLD + key] = uint16_t(wv[j] & 0xffffu);
-          sV[(ch * 8 + 2 * j + 1) * VLD + key] = uint16_t(wv[j] >> 16);
-        }
+    for (int i = 0; i < NL; ++i) {
+      const int c = tid + 256 * i, key = c / (D / 8), ch = c % (D / 8);
+      *reinterpret_cast<uint4*>(&sK[key * KLD + ch * 8]) =
+          make_uint4(kreg[4 * i], kreg[4 * i + 1], kreg[4 * i + 2], kreg[4 * i + 3]);
+      const int vch = (tid >> 6) + 4 * i;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t wv = vreg[4 * i + j];
+        sV[(vch * 8 + 2 * j) * VLD + vkey] = uint16_t(wv & 0xffffu);
+        sV[(vch * 8 + 2 * j + 1) * VLD + vkey] = uint16_t(wv >> 16);
       }
     }
     __syncthreads();
+    ORCA_PF_LOAD(k0 + BKV)
     if (k0 >= kend_wave) continue;
 
     // S^T = K Q^T for keys k0 .. k0+63 (two 32-key tiles)
@@ -324,6 +339,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     }
   }
 
+#undef ORCA_PF_LOAD
   // normalise, transpose through LDS, write the rows
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
