@@ -81,6 +81,20 @@ def source_hash(files):
     return m.hexdigest()[:16]
 
 
+def measured_mfma_util(workload):
+    """MFMA utilisation (%) of the FFN1 launch from the committed rocprofv3
+    MfmaUtil run; None when absent or the GEMM source changed since."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get("mfma_util_percent")
+    if not rec or rec.get("source_hash") != source_hash(["gemm.hip", "device.h", "kernels.h"]):
+        return None
+    vals = list(rec.get("gemm", {}).values())
+    return round(sum(vals) / len(vals), 2) if vals else None
+
+
 def measured_traffic(workload, key, files):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE runs, scaled by the plain-copy calibration; None when no
@@ -139,6 +153,18 @@ def summarize_traffic(src, workload):
                     "write_kib": {k: round(v, 1) for k, v in w.items()},
                     "fetch_bytes": sum(f.values()) * 1024 * fs,
                     "write_bytes": sum(w.values()) * 1024 * ws}
+    # MFMA utilisation (rocprofv3's MfmaUtil: MFMA busy cycles over GPU-active
+    # cycles times SIMDs), per GEMM kernel, for the FFN1 launch and the
+    # GEMMs of a whole iteration
+    util = {}
+    for what in ("gemm", "iteration"):
+        path = os.path.join(src, f"pmc_{what}_MfmaUtil", "run_counter_collection.csv")
+        if os.path.exists(path):
+            util[what] = {k: round(v, 2) for k, v in
+                          _counter_means(path, TRAFFIC_KERNELS["gemm"]).items()}
+    if util:
+        out["mfma_util_percent"] = {"source_hash": source_hash(["gemm.hip", "device.h",
+                                                                  "kernels.h"]), **util}
     dst = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
     with open(dst, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -265,6 +291,7 @@ def main():
         else:
             kname = "gemm_f32_kernel<gelu>"
         common = {"kernel": kname + " (FFN1)", "shape": [M, F, H],
+                  "mfma_util_percent_counter": measured_mfma_util(work.name),
                   "traffic": tr["bytes"] if tr else None,
                   "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
                   "algorithmic_flops": int(flops), "algorithmic_bytes": int(alg_bytes),
