@@ -79,8 +79,9 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
       kr[u] = make_uint4(0, 0, 0, 0);
       vr[u] = make_uint4(0, 0, 0, 0);
       if (ok[u]) {
-        kr[u] = *reinterpret_cast<const uint4*>(kb + (size_t)key * D);
-        vr[u] = *reinterpret_cast<const uint4*>(vb + (size_t)key * D);
+        // each cached key and value is read once per layer: stream them
+        kr[u] = load_nt16(kb + (size_t)key * D);
+        vr[u] = load_nt16(vb + (size_t)key * D);
       }
     }
     float s[U];

@@ -44,6 +44,15 @@ template <> __device__ __forceinline__ void store_f32<bf16>(bf16* p, float v) {
 }
 
 // 16 bytes of T <-> fp32 lanes (8 for bf16, 4 for fp32).
+// 16-byte load with the non-temporal hint, for data read once per launch
+// (streamed K/V, streamed weights): on MI355X a plain streaming read reaches
+// ~6.3 TB/s, with the hint ~7.1 TB/s.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 template <typename T> struct Vec16;
 template <> struct Vec16<float> {
   static constexpr int N = 4;

@@ -113,7 +113,16 @@ struct TileCfg {
   static_assert(LA * NT == BM * 8 && LB * NT == BN * 8, "tile not divisible by threads");
 };
 
-template <int EPI, int WGM, int WGN, int TI, int TJ, bool PIPE>
+template <bool NT>
+__device__ __forceinline__ uint4 load_w(const bf16* p) {
+  if constexpr (NT) return load_nt16(p);
+  else return *reinterpret_cast<const uint4*>(p);
+}
+
+// STREAM_W: W is read by one row tile only (the few-rows path), so its
+// loads carry the non-temporal hint; otherwise W panels are re-read by the
+// other row tiles through L2 and load plainly.
+template <int EPI, int WGM, int WGN, int TI, int TJ, bool PIPE, bool STREAM_W = false>
 __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && TI * TJ <= 4) ? 2 : 1)
 void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
                       const bf16* __restrict__ bias, EpiParams ep, int M, int N, int K,
@@ -162,7 +171,7 @@ void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
 #pragma unroll
   for (int i = 0; i < C::LA; ++i) ra[i] = *reinterpret_cast<const uint4*>(gA[i]);
 #pragma unroll
-  for (int i = 0; i < C::LB; ++i) rb[i] = *reinterpret_cast<const uint4*>(gB[i]);
+  for (int i = 0; i < C::LB; ++i) rb[i] = load_w<STREAM_W>(gB[i]);
 #pragma unroll
   for (int i = 0; i < C::LA; ++i) *reinterpret_cast<uint4*>(&sA[0][oA[i]]) = ra[i];
 #pragma unroll
@@ -180,7 +189,7 @@ void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
 #pragma unroll
       for (int i = 0; i < C::LA; ++i) ra[i] = *reinterpret_cast<const uint4*>(gA[i] + kn);
 #pragma unroll
-      for (int i = 0; i < C::LB; ++i) rb[i] = *reinterpret_cast<const uint4*>(gB[i] + kn);
+      for (int i = 0; i < C::LB; ++i) rb[i] = load_w<STREAM_W>(gB[i] + kn);
       __builtin_amdgcn_sched_barrier(0);
       const uint16_t* a_base = &sA[cur][a_off];
       const uint16_t* b_base = &sB[cur][b_off];
@@ -220,7 +229,7 @@ void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
     PA[4 * i] = t.x; PA[4 * i + 1] = t.y; PA[4 * i + 2] = t.z; PA[4 * i + 3] = t.w;          \
   }                                                                                          \
   _Pragma("unroll") for (int i = 0; i < C::LB; ++i) {                                        \
-    const uint4 t = *reinterpret_cast<const uint4*>(gB[i] + (KOFF));                         \
+    const uint4 t = load_w<STREAM_W>(gB[i] + (KOFF));                                        \
     PB[4 * i] = t.x; PB[4 * i + 1] = t.y; PB[4 * i + 2] = t.z; PB[4 * i + 3] = t.w;          \
   }
 #define ORCA_STORE_STAGE(PA, PB, BUF)                                                        \
@@ -381,12 +390,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 //  10: split-K (see plan_gemm)
 // (6, 7 and 8 need an even number of K steps and fall back to 3, 0 and the
 // one-step 256 x 192 form.)
-template <int EPI, int WGM, int WGN, int TI, int TJ, bool PIPE = false>
+template <int EPI, int WGM, int WGN, int TI, int TJ, bool PIPE = false, bool STREAM_W = false>
 static void launch_mfma(const void* a, const void* w, const void* bias, const EpiParams& ep, int m,
                         int n, int k, hipStream_t s, int splits = 1, int kt_per_split = 0) {
   using C = TileCfg<WGM, WGN, TI, TJ>;
   const int tiles_m = (m + C::BM - 1) / C::BM, tiles_n = (n + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WGM, WGN, TI, TJ, PIPE>),
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WGM, WGN, TI, TJ, PIPE, STREAM_W>),
                      dim3(tiles_m * tiles_n, splits), dim3(C::NT), 0, s, (const bf16*)a,
                      (const bf16*)w, (const bf16*)bias, ep, m, n, k, tiles_m,
                      kt_per_split > 0 ? kt_per_split : k / BK);
@@ -504,15 +513,15 @@ size_t linear_workspace_bytes(int dtype, int m, int n, int k) {
   return (size_t)p.splits * m * n * sizeof(float);
 }
 
-template <int WGM, int WGN, int TI, int TJ>
+template <int WGM, int WGN, int TI, int TJ, bool STREAM_W = false>
 static void launch_partial(const SplitPlan& p, const void* a, const void* w, const EpiParams& pp,
                            int m, int n, int k, hipStream_t s) {
   if (p.kt_per_split % 2 == 0 && (k / BK) % 2 == 0)
-    launch_mfma<EPI_PARTIAL, WGM, WGN, TI, TJ, true>(a, w, nullptr, pp, m, n, k, s, p.splits,
-                                                     p.kt_per_split);
+    launch_mfma<EPI_PARTIAL, WGM, WGN, TI, TJ, true, STREAM_W>(a, w, nullptr, pp, m, n, k, s,
+                                                               p.splits, p.kt_per_split);
   else
-    launch_mfma<EPI_PARTIAL, WGM, WGN, TI, TJ>(a, w, nullptr, pp, m, n, k, s, p.splits,
-                                               p.kt_per_split);
+    launch_mfma<EPI_PARTIAL, WGM, WGN, TI, TJ, false, STREAM_W>(a, w, nullptr, pp, m, n, k, s,
+                                                                p.splits, p.kt_per_split);
 }
 
 template <int EPI>
@@ -521,8 +530,9 @@ static void launch_split(const SplitPlan& p, const void* a, const void* w, const
   EpiParams pp{};
   pp.out = part;
   pp.ldo = n;
-  if (p.tile == 0) launch_partial<1, 4, 1, 1>(p, a, w, pp, m, n, k, s);
-  else if (p.tile == 1) launch_partial<1, 4, 2, 1>(p, a, w, pp, m, n, k, s);
+  // up to 64 rows are one row tile: each weight is read by one workgroup
+  if (p.tile == 0) launch_partial<1, 4, 1, 1, true>(p, a, w, pp, m, n, k, s);
+  else if (p.tile == 1) launch_partial<1, 4, 2, 1, true>(p, a, w, pp, m, n, k, s);
   else if (p.tile == 2) launch_partial<2, 2, 2, 2>(p, a, w, pp, m, n, k, s);
   else launch_partial<4, 2, 2, 4>(p, a, w, pp, m, n, k, s);
   const int threads = m * (n / 4);
