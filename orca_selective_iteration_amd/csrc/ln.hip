@@ -5,7 +5,8 @@
 // scaling run as one fused kernel.  garden.houmin.site/infra/orca 3.1.2:
 // LayerNorm mixes no tokens, so it runs on all rows of the batch at once.
 //
-// One 256-thread workgroup per row; the row stays in registers (16-byte
+// One 128-thread workgroup per row (16 per CU, so a 13B batch of 2176 rows
+// runs in one round); the row stays in registers (16-byte
 // loads, fully coalesced) between the mean pass, the centred variance pass
 // and the normalise pass, so HBM sees one read of the fp32 row and one write
 // of the output row: (4 + sizeof(T)) * H bytes per row.
@@ -15,8 +16,8 @@
 
 namespace orca {
 
-constexpr int LN_THREADS = 256;
-constexpr int LN_MAX_VEC = 12;   // float4 per thread: H <= 12288
+constexpr int LN_THREADS = 128;
+constexpr int LN_MAX_VEC = 24;   // float4 per thread: H <= 12288
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
@@ -40,7 +41,9 @@ __device__ __forceinline__ void store4(bf16* p, float4 v) {
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
 }
 
-template <typename T>
+// NV: float4 per thread, the smallest instantiation that holds the row
+// (registers beyond it would cut the workgroups resident per CU)
+template <typename T, int NV>
 __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const float* __restrict__ x,
                                                                const T* __restrict__ g,
                                                                const T* __restrict__ b,
@@ -50,10 +53,10 @@ __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const float* __re
   const int row = blockIdx.x;
   const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * hidden);
   const int nv = hidden / 4;
-  float4 v[LN_MAX_VEC];
+  float4 v[NV];
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < LN_MAX_VEC; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int c = threadIdx.x + i * LN_THREADS;
     if (c < nv) {
       v[i] = xr[c];
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const float* __re
   const float mean = block_sum(s, red) / hidden;
   float q = 0.f;
 #pragma unroll
-  for (int i = 0; i < LN_MAX_VEC; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int c = threadIdx.x + i * LN_THREADS;
     if (c < nv) {
       const float a = v[i].x - mean, bb = v[i].y - mean, cc = v[i].z - mean, d = v[i].w - mean;
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const float* __re
   }
   const float rstd = rsqrtf(block_sum(q, red) / hidden + eps);
 #pragma unroll
-  for (int i = 0; i < LN_MAX_VEC; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int c = threadIdx.x + i * LN_THREADS;
     if (c < nv) {
       const float4 gg = load4(g + c * 4), bb = load4(b + c * 4);
@@ -100,15 +103,29 @@ __global__ void from_f32_kernel(const float* __restrict__ in, T* __restrict__ ou
     store_f32(out + i, in[i]);
 }
 
+template <typename T>
+static void launch_ln_typed(const float* x, const void* g, const void* b, void* out, int rows,
+                            int hidden, float eps, hipStream_t s) {
+  const int nv = (hidden / 4 + LN_THREADS - 1) / LN_THREADS;
+#define ORCA_LN(NV)                                                                          \
+  hipLaunchKernelGGL((layernorm_kernel<T, NV>), dim3(rows), dim3(LN_THREADS), 0, s, x,       \
+                     (const T*)g, (const T*)b, (T*)out, hidden, eps)
+  if (nv <= 2) ORCA_LN(2);
+  else if (nv <= 4) ORCA_LN(4);
+  else if (nv <= 6) ORCA_LN(6);
+  else if (nv <= 8) ORCA_LN(8);
+  else if (nv <= 10) ORCA_LN(10);
+  else if (nv <= 12) ORCA_LN(12);
+  else if (nv <= 16) ORCA_LN(16);
+  else ORCA_LN(LN_MAX_VEC);
+#undef ORCA_LN
+}
+
 hipError_t launch_layernorm(int dtype, const float* x, const void* g, const void* b, void* out,
                             int rows, int hidden, float eps, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (dtype == ORCA_BF16)
-    hipLaunchKernelGGL(layernorm_kernel<bf16>, dim3(rows), dim3(LN_THREADS), 0, s, x,
-                       (const bf16*)g, (const bf16*)b, (bf16*)out, hidden, eps);
-  else
-    hipLaunchKernelGGL(layernorm_kernel<float>, dim3(rows), dim3(LN_THREADS), 0, s, x,
-                       (const float*)g, (const float*)b, (float*)out, hidden, eps);
+  if (dtype == ORCA_BF16) launch_ln_typed<bf16>(x, g, b, out, rows, hidden, eps, s);
+  else launch_ln_typed<float>(x, g, b, out, rows, hidden, eps, s);
   return hipGetLastError();
 }
 
