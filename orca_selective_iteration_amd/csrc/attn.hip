@@ -16,8 +16,9 @@
 // of the key row and of the value row (so a wave reads 64 x 16 contiguous
 // bytes per instruction), the partial dot products are summed with DPP row
 // operations, and an online softmax (base 2, running max m and sum l per
-// lane group) accumulates the value rows.  Four keys per lane group are in
-// flight per loop trip.  The lane groups, then the four waves, are merged
+// lane group) accumulates the value rows.  Eight keys per lane group are in
+// flight per loop trip, loaded with the non-temporal hint (each cached key
+// and value is read once per layer).  The lane groups, then the four waves, are merged
 // through shuffles and LDS into one (m, l, o[d]) partial per item; a second
 // kernel merges the partials of a row and writes o at the row's own offset
 // (the merge is index arithmetic: no copy).
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   constexpr int LPK = D / VEC;       // lanes per key
   constexpr int KPW = 64 / LPK;      // keys per wave per load
   constexpr int NW = 4;
-  constexpr int U = 4;
+  constexpr int U = 8;
   constexpr int STRIDE = NW * KPW;   // keys per workgroup per load
   __shared__ float s_o[NW][D];
   __shared__ float s_ml[NW][2];
