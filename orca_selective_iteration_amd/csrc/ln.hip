@@ -5,8 +5,9 @@
 // scaling run as one fused kernel.  garden.houmin.site/infra/orca 3.1.2:
 // LayerNorm mixes no tokens, so it runs on all rows of the batch at once.
 //
-// One 128-thread workgroup per row (16 per CU, so a 13B batch of 2176 rows
-// runs in one round); the row stays in registers (16-byte
+// One workgroup per row: 128 threads (up to 16 per CU, so a 13B batch of 2176
+// rows runs in one round), 256 for rows wider than 6144 (fewer registers per
+// thread); the row stays in registers (16-byte
 // loads, fully coalesced) between the mean pass, the centred variance pass
 // and the normalise pass, so HBM sees one read of the fp32 row and one write
 // of the output row: (4 + sizeof(T)) * H bytes per row.
@@ -16,9 +17,9 @@
 
 namespace orca {
 
-constexpr int LN_THREADS = 128;
-constexpr int LN_MAX_VEC = 24;   // float4 per thread: H <= 12288
+constexpr int LN_MAX_VEC = 12;   // float4 per thread: H <= 12288 at 256 threads
 
+template <int NT>
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
@@ -26,7 +27,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   if (lane == 0) red[w] = v;
   __syncthreads();
   float t = 0.f;
-  for (int i = 0; i < LN_THREADS / 64; ++i) t += red[i];
+  for (int i = 0; i < NT / 64; ++i) t += red[i];
   return t;
 }
 
@@ -41,15 +42,15 @@ __device__ __forceinline__ void store4(bf16* p, float4 v) {
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
 }
 
-// NV: float4 per thread, the smallest instantiation that holds the row
-// (registers beyond it would cut the workgroups resident per CU)
-template <typename T, int NV>
-__global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const float* __restrict__ x,
+// NT threads, NV float4 per thread: the smallest instantiation that holds
+// the row (registers beyond it would cut the workgroups resident per CU)
+template <typename T, int NT, int NV>
+__global__ __launch_bounds__(NT) void layernorm_kernel(const float* __restrict__ x,
                                                                const T* __restrict__ g,
                                                                const T* __restrict__ b,
                                                                T* __restrict__ out, int hidden,
                                                                float eps) {
-  __shared__ float red[LN_THREADS / 64];
+  __shared__ float red[NT / 64];
   const int row = blockIdx.x;
   const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * hidden);
   const int nv = hidden / 4;
@@ -57,26 +58,26 @@ __global__ __launch_bounds__(LN_THREADS) void layernorm_kernel(const float* __re
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int c = threadIdx.x + i * LN_THREADS;
+    const int c = threadIdx.x + i * NT;
     if (c < nv) {
       v[i] = xr[c];
       s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
     }
   }
-  const float mean = block_sum(s, red) / hidden;
+  const float mean = block_sum<NT>(s, red) / hidden;
   float q = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int c = threadIdx.x + i * LN_THREADS;
+    const int c = threadIdx.x + i * NT;
     if (c < nv) {
       const float a = v[i].x - mean, bb = v[i].y - mean, cc = v[i].z - mean, d = v[i].w - mean;
       q += (a * a + bb * bb) + (cc * cc + d * d);
     }
   }
-  const float rstd = rsqrtf(block_sum(q, red) / hidden + eps);
+  const float rstd = rsqrtf(block_sum<NT>(q, red) / hidden + eps);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int c = threadIdx.x + i * LN_THREADS;
+    const int c = threadIdx.x + i * NT;
     if (c < nv) {
       const float4 gg = load4(g + c * 4), bb = load4(b + c * 4);
       float4 y;
@@ -106,18 +107,19 @@ __global__ void from_f32_kernel(const float* __restrict__ in, T* __restrict__ ou
 template <typename T>
 static void launch_ln_typed(const float* x, const void* g, const void* b, void* out, int rows,
                             int hidden, float eps, hipStream_t s) {
-  const int nv = (hidden / 4 + LN_THREADS - 1) / LN_THREADS;
-#define ORCA_LN(NV)                                                                          \
-  hipLaunchKernelGGL((layernorm_kernel<T, NV>), dim3(rows), dim3(LN_THREADS), 0, s, x,       \
+  const int v4 = hidden / 4;
+#define ORCA_LN(NT, NV)                                                                      \
+  hipLaunchKernelGGL((layernorm_kernel<T, NT, NV>), dim3(rows), dim3(NT), 0, s, x,           \
                      (const T*)g, (const T*)b, (T*)out, hidden, eps)
-  if (nv <= 2) ORCA_LN(2);
-  else if (nv <= 4) ORCA_LN(4);
-  else if (nv <= 6) ORCA_LN(6);
-  else if (nv <= 8) ORCA_LN(8);
-  else if (nv <= 10) ORCA_LN(10);
-  else if (nv <= 12) ORCA_LN(12);
-  else if (nv <= 16) ORCA_LN(16);
-  else ORCA_LN(LN_MAX_VEC);
+  if (v4 <= 128 * 2) ORCA_LN(128, 2);
+  else if (v4 <= 128 * 4) ORCA_LN(128, 4);
+  else if (v4 <= 128 * 6) ORCA_LN(128, 6);
+  else if (v4 <= 128 * 8) ORCA_LN(128, 8);
+  else if (v4 <= 128 * 10) ORCA_LN(128, 10);
+  else if (v4 <= 128 * 12) ORCA_LN(128, 12);
+  else if (v4 <= 256 * 8) ORCA_LN(256, 8);
+  else if (v4 <= 256 * 10) ORCA_LN(256, 10);
+  else ORCA_LN(256, LN_MAX_VEC);
 #undef ORCA_LN
 }
 

@@ -44,7 +44,10 @@ def host(t):
 
 @pytest.mark.parametrize("dtype,rows,hidden", [
     ("f32", 7, 64), ("f32", 5, 12288), ("bf16", 37, 1024), ("bf16", 130, 5120),
-    ("bf16", 3, 12288), ("bf16", 1, 64)])
+    ("bf16", 3, 12288), ("bf16", 1, 64),
+    # widths at and past the register-array sizes the launcher picks from
+    ("bf16", 9, 6144), ("bf16", 17, 6148), ("bf16", 5, 2052), ("f32", 3, 10244),
+    ("f32", 11, 4100)])
 def test_layernorm(dtype, rows, hidden):
     print(f"case layernorm {dtype} rows={rows} hidden={hidden}", flush=True)
     rng = np.random.default_rng(rows * 7 + hidden)
