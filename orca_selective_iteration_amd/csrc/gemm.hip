@@ -454,6 +454,23 @@ static double cost_tiled(int v, int m, int n) {
     default: return ceil_div_l(ceil_div_l(m, 128) * ceil_div_l(n, 128), 2 * NUM_CU) * 32768.0 / 0.84;
   }
 }
+// The tiled variant of least estimated cost; another tile than 256 x 256
+// only on a predicted gain of 3% or more (the model is coarse; in a full
+// iteration the 175B shapes, where 256 x 192 was predicted 1% faster, ran 1%
+// slower).
+static int best_tiled(int m, int n, double& best) {
+  int v = 6;
+  best = cost_tiled(6, m, n) * 0.97;
+  for (int c : {8, 7}) {
+    const double e = cost_tiled(c, m, n);
+    if (e < best) {
+      best = e;
+      v = c;
+    }
+  }
+  return v;
+}
+
 // 256 x 256 tiles with K split by 2-4 (each split at least 40 K steps; its
 // partial sums are written and read back once, charged at 15%).
 static double cost_big_split(int m, int n, int k, SplitPlan& p) {
@@ -483,18 +500,8 @@ static int plan_gemm(int m, int n, int k, SplitPlan& split) {
   if (pinned >= 0 && pinned != 10) return pinned;
   if (m >= 1 && k % BK == 0 && n % 4 == 0) {
     if (few_rows_plan(m, n, k, split)) return 10;
-    // another tile only on a predicted gain of 3% or more over 256 x 256
-    // (the model is coarse; in a full iteration the 175B shapes, where
-    // 256 x 192 was predicted 1% faster, ran 1% slower)
-    int v = 6;
-    double best = cost_tiled(6, m, n) * 0.97;
-    for (int c : {8, 7}) {
-      const double e = cost_tiled(c, m, n);
-      if (e < best) {
-        best = e;
-        v = c;
-      }
-    }
+    double best;
+    const int v = best_tiled(m, n, best);
     SplitPlan bs;
     if (cost_big_split(m, n, k, bs) < best || pinned == 10) {
       if (bs.splits > 1 && bs.splits <= SPLIT_MAX_SPLITS) {
@@ -552,7 +559,8 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
         launch_split<EPI>(sp, a, w, bias, ep, static_cast<float*>(ws), m, n, k, s);
         return;
       }
-      v = cost_tiled(8, m, n) < cost_tiled(6, m, n) ? 8 : 7;   // no room for the partials
+      double c;
+      v = best_tiled(m, n, c);   // no room for the partials: the best tiled launch
     }
     switch (v) {
       case 0: launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;
