@@ -213,13 +213,15 @@ typedef enum {
 /* acc[m][n] = sum_k a[m][k] * w[n][k] on a device [m][k], w device [n][k],
  * bias device [n] (all `dtype`), then the epilogue.  m >= 0; n % 64 == 0 and
  * k % 64 == 0.  bf16 runs on the MFMA units.
- * workspace: device scratch owned by the caller, may be NULL.  For bf16 and
- * m <= 64 rows (batches made mostly of increment rows: the weights are
- * streamed once and the arithmetic is light) a split-K path runs when
- * ws_bytes >= orca_op_linear_workspace_bytes(dtype, m, n, k); it writes fp32
- * partial sums there.  Otherwise the tiled path runs and the workspace is
- * not touched.  Both paths accumulate in fp32; only the summation order
- * differs. */
+ * workspace: device scratch owned by the caller, may be NULL.  For bf16
+ * problems whose output tiles are too few to fill the GPU (chiefly batches of
+ * few rows, made mostly of increment rows: the weights are streamed once
+ * and the arithmetic is light) a split-K path runs when
+ * ws_bytes >= orca_op_linear_workspace_bytes(dtype, m, n, k) > 0; it writes
+ * fp32 partial sums there.  Otherwise the tiled path runs and the workspace
+ * is not touched.  Both paths accumulate in fp32; only the summation order
+ * differs.  orca_op_linear_workspace_bytes returns 0 where split-K does not
+ * apply (fp32, or enough tiles). */
 size_t orca_op_linear_workspace_bytes(int32_t dtype, int32_t m, int32_t n, int32_t k);
 orca_status orca_op_linear(int32_t dtype, int32_t epilogue, const void* a, const void* w,
                            const void* bias, void* out, int32_t m, int32_t n, int32_t k,
