@@ -216,6 +216,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   // qpos = kv_len + qi (kv_len: prompt tokens cached by earlier chunks)
   const int qi = it.q0 + w * 32 + col;
   const int qpos = rq.kv_len + qi;
+  const int qmin = rq.kv_len + it.q0 + w * 32;   // the wave's first query position
   const int qrow = rq.q_offset + min(qi, it.q1 - 1);
   bf16x8_t qf[D / 16];
   {
@@ -266,11 +267,16 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
       *reinterpret_cast<uint4*>(&sK[key * KLD + ch * 8]) =
           make_uint4(kreg[4 * i], kreg[4 * i + 1], kreg[4 * i + 2], kreg[4 * i + 3]);
       const int vch = (tid >> 6) + 4 * i;
+      // V^T: this lane holds dims d, d+1 of key vkey in each word; with the
+      // neighbouring key's word (lane ^ 1, a DPP move) an even lane writes
+      // row d and an odd lane row d+1, two consecutive keys per 32-bit store
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t wv = vreg[4 * i + j];
-        sV[(vch * 8 + 2 * j) * VLD + vkey] = uint16_t(wv & 0xffffu);
-        sV[(vch * 8 + 2 * j + 1) * VLD + vkey] = uint16_t(wv >> 16);
+        const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wv, 0xB1, 0xF, 0xF, false);
+        const uint32_t word = (vkey & 1) ? ((nb >> 16) | (wv & 0xffff0000u))
+                                         : ((wv & 0xffffu) | (nb << 16));
+        *reinterpret_cast<uint32_t*>(&sV[(vch * 8 + 2 * j + (vkey & 1)) * VLD + (vkey & ~1)]) = word;
       }
     }
     __syncthreads();
@@ -290,19 +296,30 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
       }
     }
-    // causal mask, scale, running max
+    // causal mask, only on blocks reaching past the wave's first query or
+    // the last key (wave-uniform test); running max on the raw scores, the
+    // scale folded into the exponent below
     float mx = NEG_BIG;
+    if (k0 + BKV - 1 <= qmin && k0 + BKV <= kend) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool vis = key <= qpos && key < kend;
-        s[t][r] = vis ? s[t][r] * sc : NEG_BIG;
-        mx = fmaxf(mx, s[t][r]);
-      }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = key <= qpos && key < kend;
+          s[t][r] = vis ? s[t][r] : NEG_BIG;
+          mx = fmaxf(mx, s[t][r]);
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
+    // every query sees key 0 in the first block, so m_run is finite from
+    // then on and a masked score's exponent is far below it (p = 0)
+    const float m_new = fmaxf(m_run, mx * sc);
     const float corr = exp2f(m_run - m_new);
     m_run = m_new;
     l_run *= corr;
@@ -314,7 +331,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = s[t][r] > 0.5f * NEG_BIG ? exp2f(s[t][r] - m_new) : 0.f;
+        const float p = exp2f(fmaf(s[t][r], sc, -m_new));
         s[t][r] = p;
         l_run += p;
       }
