@@ -119,6 +119,37 @@ __device__ __forceinline__ uint4 load_w(const bf16* p) {
   else return *reinterpret_cast<const uint4*>(p);
 }
 
+// The epilogue of one wave's (32*TI) x (32*TJ) accumulators whose first
+// row is m0 and first column n0.  32x32 accumulator layout: lane holds
+// column lane%32 and rows 8*(r/4) + 4*(lane/32) + r%4 for its 16 registers r.
+template <int EPI, int TI, int TJ>
+__device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[TI][TJ],
+                                                const bf16* __restrict__ bias,
+                                                const EpiParams& ep, int M, int N, int m0,
+                                                int n0, int lane) {
+  using OutT = typename std::conditional<EPI == ORCA_EPI_BIAS_RESID || EPI == EPI_PARTIAL, float,
+                                         bf16>::type;
+  const int fr = lane & 31;
+  float bn[TJ];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+    bn[j] = EPI == EPI_PARTIAL ? 0.f : load_f32(bias + min(n0 + j * 32 + fr, N - 1));
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int n = n0 + j * 32 + fr;
+    if (n >= N) continue;
+    const EpiCol<OutT, EPI> col(ep, n);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m < M) col.store(m, EPI == EPI_QKV ? ep.qkv.row_dst[m] : 0, acc[i][j][r] + bn[j]);
+      }
+    }
+  }
+}
+
 // STREAM_W: W is read by one row tile only (the few-rows path), so its
 // loads carry the non-temporal hint; otherwise W panels are re-read by the
 // other row tiles through L2 and load plainly.
@@ -270,29 +301,133 @@ void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
 #undef ORCA_STORE_STAGE
   }
 
-  // 32x32 accumulator layout: lane holds column lane%32 and rows
-  // 8*(r/4) + 4*(lane/32) + r%4 for its 16 registers r.
-  using OutT = typename std::conditional<EPI == ORCA_EPI_BIAS_RESID || EPI == EPI_PARTIAL, float,
-                                         bf16>::type;
-  float bn[TJ];
+  store_wave_tile<EPI, TI, TJ>(acc, bias, ep, M, N, tm * C::BM + wm * 32 * TI,
+                               tn * C::BN + wn * 32 * TJ, lane);
+}
+
+// ------------------------------------------------- wave-specialised 256 x 256
+
+// 256 x 256 tile with the work split by wave: eight MFMA waves (a 4 x 2 grid,
+// 64 x 128 each, as in the tile above) only read LDS and issue MFMAs, and
+// four loader waves move the K steps from global memory through registers
+// into the double-buffered LDS stage.  A loader holds two K steps in
+// registers, so a load has two whole steps to arrive before its data is
+// written to LDS, and the MFMA waves never wait on global memory.  All
+// twelve waves meet at one barrier per K step: after it the MFMA waves read
+// the buffer written before it, while the loaders fill the other one.
+// Needs an even number of K steps and element offsets below 2^31.
+constexpr int WS_THREADS = 768, WS_LOADERS = 256, WS_MIN_K = 8192;
+
+template <int EPI>
+__global__ __launch_bounds__(WS_THREADS, 1)
+void gemm_ws_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
+                    const bf16* __restrict__ bias, EpiParams ep, int M, int N, int K,
+                    int tiles_m) {
+  constexpr int BM = 256, BN = 256, TI = 2, TJ = 4;
+  constexpr int LD = BM * 8 / WS_LOADERS;   // 16-byte chunks per loader lane and operand
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDK];
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int tm = logical % tiles_m, tn = logical / tiles_m;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform role (a scalar branch: each path runs its own barriers)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int KT = K / BK;
+
+  if (wave >= 8) {
+    const int lt = tid - 8 * 64, ch = lt & 7;
+    // byte offsets from the operand base (a uniform base plus a 32-bit
+    // offset per load keeps the loader's addresses to one register each)
+    uint32_t offA[LD], offB[LD];
 #pragma unroll
-  for (int j = 0; j < TJ; ++j)
-    bn[j] = EPI == EPI_PARTIAL ? 0.f
-                               : load_f32(bias + min(tn * C::BN + wn * 32 * TJ + j * 32 + fr, N - 1));
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int n = tn * C::BN + wn * 32 * TJ + j * 32 + fr;
-    if (n >= N) continue;
-    const EpiCol<OutT, EPI> col(ep, n);
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = tm * C::BM + wm * 32 * TI + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m < M) col.store(m, EPI == EPI_QKV ? ep.qkv.row_dst[m] : 0, acc[i][j][r] + bn[j]);
-      }
+    for (int i = 0; i < LD; ++i) {
+      const int row = (lt >> 3) + 32 * i;
+      offA[i] = (uint32_t)(min(tm * BM + row, M - 1) * K + ch * 8) * 2u;
+      offB[i] = (uint32_t)(min(tn * BN + row, N - 1) * K + ch * 8) * 2u;
     }
+    const int oL = (lt >> 3) * LDK + ch * 8;   // chunk i lands 32 rows further down
+    typedef uint32_t Stage __attribute__((ext_vector_type(8 * LD)));
+    Stage s0, s1;
+#define ORCA_WS_LOAD(S, KS)                                                                   \
+  {                                                                                           \
+    const char* bA = reinterpret_cast<const char*>(A) + (size_t)(KS) * BK * 2;                \
+    const char* bB = reinterpret_cast<const char*>(W) + (size_t)(KS) * BK * 2;                \
+    _Pragma("unroll") for (int i = 0; i < LD; ++i) {                                          \
+      const uint4 a = *reinterpret_cast<const uint4*>(bA + offA[i]);                          \
+      S[4 * i] = a.x; S[4 * i + 1] = a.y; S[4 * i + 2] = a.z; S[4 * i + 3] = a.w;             \
+    }                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < LD; ++i) {                                          \
+      const uint4 b = *reinterpret_cast<const uint4*>(bB + offB[i]);                          \
+      S[4 * LD + 4 * i] = b.x; S[4 * LD + 4 * i + 1] = b.y;                                   \
+      S[4 * LD + 4 * i + 2] = b.z; S[4 * LD + 4 * i + 3] = b.w;                               \
+    }                                                                                         \
   }
+#define ORCA_WS_STORE(S, BUF)                                                                 \
+  {                                                                                           \
+    _Pragma("unroll") for (int i = 0; i < LD; ++i)                                            \
+        *reinterpret_cast<uint4*>(&sA[BUF][oL + i * 32 * LDK]) =                              \
+            make_uint4(S[4 * i], S[4 * i + 1], S[4 * i + 2], S[4 * i + 3]);                   \
+    _Pragma("unroll") for (int i = 0; i < LD; ++i)                                            \
+        *reinterpret_cast<uint4*>(&sB[BUF][oL + i * 32 * LDK]) =                              \
+            make_uint4(S[4 * LD + 4 * i], S[4 * LD + 4 * i + 1], S[4 * LD + 4 * i + 2],       \
+                       S[4 * LD + 4 * i + 3]);                                                \
+  }
+    ORCA_WS_LOAD(s0, 0)
+    ORCA_WS_LOAD(s1, min(1, KT - 1))
+    ORCA_WS_STORE(s0, 0)
+    ORCA_WS_LOAD(s0, min(2, KT - 1))
+    __syncthreads();
+    // at the barrier ending step kt the buffer of step kt+1 is full; the
+    // registers then take step kt+3 (clamped: the last trips re-read)
+    for (int kt = 0; kt < KT; kt += 2) {
+      ORCA_WS_STORE(s1, 1)
+      ORCA_WS_LOAD(s1, min(kt + 3, KT - 1))
+      __syncthreads();
+      ORCA_WS_STORE(s0, 0)
+      ORCA_WS_LOAD(s0, min(kt + 4, KT - 1))
+      __syncthreads();
+    }
+#undef ORCA_WS_LOAD
+#undef ORCA_WS_STORE
+    return;
+  }
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  const int a_off = (wm * 32 * TI + fr) * LDK + fk, b_off = (wn * 32 * TJ + fr) * LDK + fk;
+  f32x16_t acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#define ORCA_WS_COMPUTE(BUF)                                                                  \
+  {                                                                                           \
+    const uint16_t* a_base = &sA[BUF][a_off];                                                 \
+    const uint16_t* b_base = &sB[BUF][b_off];                                                 \
+    _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks) {                                  \
+      bf16x8_t a[TI], b[TJ];                                                                  \
+      _Pragma("unroll") for (int i = 0; i < TI; ++i) a[i] =                                   \
+          *reinterpret_cast<const bf16x8_t*>(a_base + i * 32 * LDK + ks * 16);                \
+      _Pragma("unroll") for (int j = 0; j < TJ; ++j) b[j] =                                   \
+          *reinterpret_cast<const bf16x8_t*>(b_base + j * 32 * LDK + ks * 16);                \
+      _Pragma("unroll") for (int i = 0; i < TI; ++i)                                          \
+          _Pragma("unroll") for (int j = 0; j < TJ; ++j) acc[i][j] =                          \
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);        \
+    }                                                                                         \
+  }
+  __syncthreads();
+  for (int kt = 0; kt < KT; kt += 2) {
+    ORCA_WS_COMPUTE(0)
+    __syncthreads();
+    ORCA_WS_COMPUTE(1)
+    __syncthreads();
+  }
+#undef ORCA_WS_COMPUTE
+  store_wave_tile<EPI, TI, TJ>(acc, bias, ep, M, N, tm * BM + wm * 32 * TI, tn * BN + wn * 32 * TJ,
+                               lane);
 }
 
 // ---------------------------------------------------------------- few rows
@@ -495,7 +630,7 @@ static int plan_gemm(int m, int n, int k, SplitPlan& split) {
   int pinned = -1;
   if (const char* f = getenv("ORCA_GEMM_VARIANT")) {
     const int v = atoi(f);
-    if (v == 0 || v == 3 || v == 6 || v == 7 || v == 8 || v == 10) pinned = v;
+    if (v == 0 || v == 3 || v == 6 || v == 7 || v == 8 || v == 10 || v == 11) pinned = v;
   }
   if (pinned >= 0 && pinned != 10) return pinned;
   if (m >= 1 && k % BK == 0 && n % 4 == 0) {
@@ -509,6 +644,9 @@ static int plan_gemm(int m, int n, int k, SplitPlan& split) {
         return 10;
       }
     }
+    // long K: the wave-specialised 256 x 256 form (1.5-6% faster on the
+    // 175B layer shapes, K = 12288 and 49152; no gain at K = 5120)
+    if (v == 6 && k >= WS_MIN_K) return 11;
     return v;
   }
   return 7;
@@ -565,6 +703,15 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
     switch (v) {
       case 0: launch_mfma<EPI, 2, 2, 2, 2>(a, w, bias, ep, m, n, k, s); break;
       case 3: launch_mfma<EPI, 4, 2, 2, 4>(a, w, bias, ep, m, n, k, s); break;
+      case 11:
+        if ((k / BK) % 2 == 0 && (long)std::max(m, n) * k < (1L << 31)) {
+          const int tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
+          hipLaunchKernelGGL(gemm_ws_kernel<EPI>, dim3(tiles_m * tiles_n), dim3(WS_THREADS), 0, s,
+                             (const bf16*)a, (const bf16*)w, (const bf16*)bias, ep, m, n, k,
+                             tiles_m);
+          break;
+        }
+        [[fallthrough]];   // odd K steps or offsets past 2^31: the 256 x 256 form
       case 6:
         if ((k / BK) % 2 == 0) launch_mfma<EPI, 4, 2, 2, 4, true>(a, w, bias, ep, m, n, k, s);
         else launch_mfma<EPI, 4, 2, 2, 4>(a, w, bias, ep, m, n, k, s);
