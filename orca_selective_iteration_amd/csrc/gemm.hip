@@ -43,10 +43,14 @@ struct EpiParams {
 
 __device__ __forceinline__ float gelu_tanh(float v) {
   // 0.5 v (1 + tanh(u)), u = sqrt(2/pi) (v + 0.044715 v^3)  (Hendrycks &
-  // Gimpel); 1 + tanh(u) = 2 - 2 / (exp(2u) + 1), exact at both limits.
-  const float k0 = 0.7978845608028654f;
-  const float u = k0 * (v + 0.044715f * v * v * v);
-  return v * (1.f - 1.f / (__expf(2.f * u) + 1.f));
+  // Gimpel).  With 1 + tanh(u) = 2 - 2 / (e + 1), e = exp(2u) = 2^(2u log2 e):
+  // gelu = v - v / (e + 1), exact at both limits (e -> 0 gives 0, e -> inf
+  // gives v).  The hardware exp2 and reciprocal (about 1 ulp each) replace
+  // the correctly rounded division, which costs nine instructions.
+  const float c1 = 2.f * 0.7978845608028654f * 1.4426950408889634f;   // 2 sqrt(2/pi) log2(e)
+  const float c3 = c1 * 0.044715f;
+  const float e = __builtin_amdgcn_exp2f(v * fmaf(c3, v * v, c1));
+  return fmaf(-v, __builtin_amdgcn_rcpf(e + 1.f), v);
 }
 
 // One output column of a Linear layer, fixed per lane before the epilogue:
