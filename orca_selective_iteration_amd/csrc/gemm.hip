@@ -126,7 +126,7 @@ __device__ __forceinline__ uint4 load_w(const bf16* p) {
 // The epilogue of one wave's (32*TI) x (32*TJ) accumulators whose first
 // row is m0 and first column n0.  32x32 accumulator layout: lane holds
 // column lane%32 and rows 8*(r/4) + 4*(lane/32) + r%4 for its 16 registers r.
-template <int EPI, int TI, int TJ>
+template <int EPI, int TI, int TJ, int RB = 16>
 __device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[TI][TJ],
                                                 const bf16* __restrict__ bias,
                                                 const EpiParams& ep, int M, int N, int m0,
@@ -138,6 +138,59 @@ __device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[TI][TJ],
 #pragma unroll
   for (int j = 0; j < TJ; ++j)
     bn[j] = EPI == EPI_PARTIAL ? 0.f : load_f32(bias + min(n0 + j * 32 + fr, N - 1));
+  if constexpr (EPI == ORCA_EPI_BIAS_RESID) {
+    // read-modify-write of the fp32 residual.  Element by element the
+    // compiler keeps every read behind the previous write (it cannot prove
+    // that they do not alias) and the epilogue becomes a chain of memory
+    // round trips; so a wave whose tile lies inside the matrix issues RB
+    // reads before their writes, addressed as a wave-uniform row base plus
+    // one per-lane 32-bit offset (few registers: the kernels run close to
+    // their register limit).  Edge waves, and RB = 0, take the element-wise
+    // path.
+    float* const out = static_cast<float*>(ep.out);
+    int ldo = ep.ldo;
+    // opaque to the optimiser: keeps the address arithmetic here instead of
+    // hoisted above the K loop, where it would hold registers through it
+    asm volatile("" : "+s"(ldo));
+    if (RB > 0 && m0 + 32 * TI <= M && n0 + 32 * TJ <= N) {
+      const uint32_t loff = ((uint32_t)((lane >> 5) * 4) * ldo + fr) * 4u;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int r0 = 0; r0 < 16; r0 += (RB > 0 ? RB : 16)) {
+            float old[RB > 0 ? RB : 1];
+#pragma unroll
+            for (int r = r0; r < r0 + RB; ++r) {
+              const char* row = reinterpret_cast<const char*>(
+                  out + (size_t)(m0 + i * 32 + (r >> 2) * 8 + (r & 3)) * ldo + n0 + j * 32);
+              old[r - r0] = *reinterpret_cast<const float*>(row + loff);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = r0; r < r0 + RB; ++r) {
+              char* row = reinterpret_cast<char*>(
+                  out + (size_t)(m0 + i * 32 + (r >> 2) * 8 + (r & 3)) * ldo + n0 + j * 32);
+              *reinterpret_cast<float*>(row + loff) = old[r - r0] + (acc[i][j][r] + bn[j]);
+            }
+          }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int n = n0 + j * 32 + fr;
+        if (n >= N) continue;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            if (m < M) out[(size_t)m * ldo + n] += acc[i][j][r] + bn[j];
+          }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
     const int n = n0 + j * 32 + fr;
@@ -430,8 +483,10 @@ void gemm_ws_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
     __syncthreads();
   }
 #undef ORCA_WS_COMPUTE
-  store_wave_tile<EPI, TI, TJ>(acc, bias, ep, M, N, tm * BM + wm * 32 * TI, tn * BN + wn * 32 * TJ,
-                               lane);
+  // element by element (RB = 0): at 168 registers the batched residual
+  // path spills
+  store_wave_tile<EPI, TI, TJ, 0>(acc, bias, ep, M, N, tm * BM + wm * 32 * TI,
+                                  tn * BN + wn * 32 * TJ, lane);
 }
 
 // ---------------------------------------------------------------- few rows
