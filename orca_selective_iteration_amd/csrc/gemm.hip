@@ -192,16 +192,27 @@ __device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[TI][TJ],
     return;
   }
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int n = n0 + j * 32 + fr;
-    if (n >= N) continue;
-    const EpiCol<OutT, EPI> col(ep, n);
+  for (int i = 0; i < TI; ++i) {
+    // the pool slots of the sixteen rows, read together before any write
+    // (read one by one between the writes, each is a round trip; RB = 0
+    // keeps that form, which needs fewer registers)
+    int dst[16];
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      dst[r] = EPI == EPI_QKV && RB > 0 ? ep.qkv.row_dst[min(m, M - 1)] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int n = n0 + j * 32 + fr;
+      if (n >= N) continue;
+      const EpiCol<OutT, EPI> col(ep, n);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m < M) col.store(m, EPI == EPI_QKV ? ep.qkv.row_dst[m] : 0, acc[i][j][r] + bn[j]);
+        if (m < M)
+          col.store(m, EPI == EPI_QKV && RB == 0 ? ep.qkv.row_dst[m] : dst[r],
+                    acc[i][j][r] + bn[j]);
       }
     }
   }
@@ -484,7 +495,7 @@ void gemm_ws_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
   }
 #undef ORCA_WS_COMPUTE
   // element by element (RB = 0): at 168 registers the batched residual
-  // path spills
+  // and pool-slot reads spill
   store_wave_tile<EPI, TI, TJ, 0>(acc, bias, ep, M, N, tm * BM + wm * 32 * TI,
                                   tn * BN + wn * 32 * TJ, lane);
 }
@@ -518,10 +529,13 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   }
   const int dst = EPI == EPI_QKV ? ep.qkv.row_dst[m] : 0;
   const float vv[4] = {v.x, v.y, v.z, v.w};
+  float bb[4];   // the bias read before the first write
+#pragma unroll
+  for (int c = 0; c < 4; ++c) bb[c] = load_f32(bias + n + c);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const EpiCol<OutT, EPI> col(ep, n + c);
-    col.store(m, dst, vv[c] + load_f32(bias + n + c));
+    col.store(m, dst, vv[c] + bb[c]);
   }
 }
 
