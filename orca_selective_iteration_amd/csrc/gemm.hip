@@ -631,10 +631,14 @@ static void set_splits(int kt, int splits, SplitPlan& p) {
 static long ceil_div_l(long a, long b) { return (a + b - 1) / b; }
 
 // Few rows (up to SPLIT_MAX_M) whose 32/64/128-row tiles are too few to fill
-// the GPU: split K so the grid fills one round of resident workgroups (two
-// per CU, bounded by LDS; more measured no faster), rounded down: every
-// workgroup streams the same share of K, and a second, mostly idle round
-// would cost as much as the first.
+// the GPU: split K.  A CU streams about as fast with one of these
+// workgroups as with two, so the time goes as the rounds of NUM_CU
+// workgroups times the K steps of one split; the split count minimises
+// that, ties going to fewer splits (each split writes and re-reads an fp32
+// partial plane), within one round of resident workgroups (two per CU,
+// bounded by LDS).  At 64 rows of the 13B layer this gives 2 splits for
+// QKV, 6 for the output projection and FFN2, 3 for FFN1 (measured: 2 and
+// 6 beat the 4-12 splits that fill 512 slots by 8-15%; 3 beats 2 and 4).
 static bool few_rows_plan(int m, int n, int k, SplitPlan& p) {
   if (m > env_int("ORCA_SPLIT_MAX_M", SPLIT_MAX_M)) return false;
   const int kt = k / BK;
@@ -645,7 +649,21 @@ static bool few_rows_plan(int m, int n, int k, SplitPlan& p) {
   const int resident = NUM_CU * std::max(1, std::min(2, LDS_PER_CU / lds));
   const int target = std::max(1, env_int("ORCA_SPLIT_TARGET", resident));
   if (2 * p.tiles > target) return false;   // enough tiles already
-  set_splits(kt, std::max(1, std::min({target / p.tiles, SPLIT_MAX_SPLITS, std::max(1, kt / 4)})), p);
+  SplitPlan best = p;
+  best.splits = 1;
+  best.kt_per_split = kt;
+  long best_cost = ceil_div_l(p.tiles, NUM_CU) * (long)kt;
+  for (int sp = 2; sp <= std::min(SPLIT_MAX_SPLITS, std::max(1, kt / 4)); ++sp) {
+    SplitPlan q = p;
+    set_splits(kt, sp, q);
+    if ((long)p.tiles * q.splits > target) break;
+    const long cost = ceil_div_l((long)p.tiles * q.splits, NUM_CU) * q.kt_per_split;
+    if (cost < best_cost) {
+      best = q;
+      best_cost = cost;
+    }
+  }
+  p = best;
   return p.splits > 1;
 }
 
