@@ -54,15 +54,23 @@ __global__ __launch_bounds__(NT) void layernorm_kernel(const float* __restrict__
   const int row = blockIdx.x;
   const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * hidden);
   const int nv = hidden / 4;
-  float4 v[NV];
+  // every load is issued before the first use, without branches (a chunk
+  // past the row's end re-reads the last one and is zeroed): behind a
+  // per-chunk branch each load waited for the one before.  Gamma and beta
+  // are read with the row, so their latency hides behind the reductions.
+  float4 v[NV], gg[NV], bb[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = min((int)threadIdx.x + i * NT, nv - 1);
+    v[i] = xr[c];
+    gg[i] = load4(g + c * 4);
+    bb[i] = load4(b + c * 4);
+  }
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int c = threadIdx.x + i * NT;
-    if (c < nv) {
-      v[i] = xr[c];
-      s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
-    }
+    if ((int)threadIdx.x + i * NT >= nv) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   }
   const float mean = block_sum<NT>(s, red) / hidden;
   float q = 0.f;
@@ -70,8 +78,8 @@ __global__ __launch_bounds__(NT) void layernorm_kernel(const float* __restrict__
   for (int i = 0; i < NV; ++i) {
     const int c = threadIdx.x + i * NT;
     if (c < nv) {
-      const float a = v[i].x - mean, bb = v[i].y - mean, cc = v[i].z - mean, d = v[i].w - mean;
-      q += (a * a + bb * bb) + (cc * cc + d * d);
+      const float a = v[i].x - mean, e = v[i].y - mean, cc = v[i].z - mean, d = v[i].w - mean;
+      q += (a * a + e * e) + (cc * cc + d * d);
     }
   }
   const float rstd = rsqrtf(block_sum<NT>(q, red) / hidden + eps);
@@ -79,12 +87,11 @@ __global__ __launch_bounds__(NT) void layernorm_kernel(const float* __restrict__
   for (int i = 0; i < NV; ++i) {
     const int c = threadIdx.x + i * NT;
     if (c < nv) {
-      const float4 gg = load4(g + c * 4), bb = load4(b + c * 4);
       float4 y;
-      y.x = (v[i].x - mean) * rstd * gg.x + bb.x;
-      y.y = (v[i].y - mean) * rstd * gg.y + bb.y;
-      y.z = (v[i].z - mean) * rstd * gg.z + bb.z;
-      y.w = (v[i].w - mean) * rstd * gg.w + bb.w;
+      y.x = (v[i].x - mean) * rstd * gg[i].x + bb[i].x;
+      y.y = (v[i].y - mean) * rstd * gg[i].y + bb[i].y;
+      y.z = (v[i].z - mean) * rstd * gg[i].z + bb[i].z;
+      y.w = (v[i].w - mean) * rstd * gg[i].w + bb[i].w;
       store4(out + (size_t)row * hidden + c * 4, y);
     }
   }
