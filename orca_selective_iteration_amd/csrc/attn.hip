@@ -160,15 +160,30 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const SplitRow sr = a.srows[blockIdx.x];
   const int h = blockIdx.y;
   for (int t = threadIdx.x; t < D; t += blockDim.x) {
-    float mx = NEG_BIG;
-    for (int i = 0; i < sr.item_count; ++i)
-      mx = fmaxf(mx, a.part_ml[((size_t)(sr.item_begin + i) * a.heads + h) * 2]);
-    float lt = 0.f, ot = 0.f;
-    for (int i = 0; i < sr.item_count; ++i) {
-      const size_t pi = (size_t)(sr.item_begin + i) * a.heads + h;
-      const float c = exp2f(a.part_ml[pi * 2] - mx);
-      lt += a.part_ml[pi * 2 + 1] * c;
-      ot += a.part_o[pi * D + t] * c;
+    // one pass with a running max, four partials per trip, all their loads
+    // issued before any is used (a clamped index re-reads the last partial
+    // and is skipped): a loop trip per partial made each a round trip
+    float mx = NEG_BIG, lt = 0.f, ot = 0.f;
+    for (int i0 = 0; i0 < sr.item_count; i0 += 4) {
+      float pm[4], pl[4], po[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const size_t pi =
+            (size_t)(sr.item_begin + min(i0 + u, sr.item_count - 1)) * a.heads + h;
+        pm[u] = a.part_ml[pi * 2];
+        pl[u] = a.part_ml[pi * 2 + 1];
+        po[u] = a.part_o[pi * D + t];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        // a select, not a branch: behind a branch the loads sink into it
+        const bool on = i0 + u < sr.item_count;
+        const float mn = fmaxf(mx, pm[u]);
+        const float c0 = exp2f(mx - mn), c1 = exp2f(pm[u] - mn);
+        lt = on ? lt * c0 + pl[u] * c1 : lt;
+        ot = on ? ot * c0 + po[u] * c1 : ot;
+        mx = on ? mn : mx;
+      }
     }
     store_f32((T*)a.o + (size_t)sr.row * a.hidden + h * D + t, ot / lt);
   }

@@ -521,17 +521,39 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= M * n4) return;
   const int m = idx / n4, n = (idx - m * n4) * 4;
-  const size_t stride = (size_t)M * N;
-  float4 v = *reinterpret_cast<const float4*>(part + (size_t)m * N + n);
-  for (int s = 1; s < splits; ++s) {
-    const float4 t = *reinterpret_cast<const float4*>(part + s * stride + (size_t)m * N + n);
-    v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
-  }
-  const int dst = EPI == EPI_QKV ? ep.qkv.row_dst[m] : 0;
-  const float vv[4] = {v.x, v.y, v.z, v.w};
+  const size_t stride = (size_t)M * N, base = (size_t)m * N + n;
   float bb[4];   // the bias read before the first write
 #pragma unroll
   for (int c = 0; c < 4; ++c) bb[c] = load_f32(bias + n + c);
+  const int dst = EPI == EPI_QKV ? ep.qkv.row_dst[m] : 0;
+  float4 old = make_float4(0.f, 0.f, 0.f, 0.f);   // the residual, read up front
+  if constexpr (EPI == ORCA_EPI_BIAS_RESID)
+    old = *reinterpret_cast<const float4*>(static_cast<const float*>(ep.out) +
+                                           (size_t)m * ep.ldo + n);
+  // the planes are read four at a time, all four issued before any is
+  // added (a clamped index re-reads the last plane and is not added): one
+  // load per loop trip made every plane a separate round trip
+  float4 v = *reinterpret_cast<const float4*>(part + base);
+  for (int s0 = 1; s0 < splits; s0 += 4) {
+    float4 t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      t[u] = *reinterpret_cast<const float4*>(part + min(s0 + u, splits - 1) * stride + base);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      // a select, not a branch: behind a branch the load sinks into it
+      const bool on = s0 + u < splits;
+      v.x += on ? t[u].x : 0.f; v.y += on ? t[u].y : 0.f;
+      v.z += on ? t[u].z : 0.f; v.w += on ? t[u].w : 0.f;
+    }
+  }
+  if constexpr (EPI == ORCA_EPI_BIAS_RESID) {
+    *reinterpret_cast<float4*>(static_cast<float*>(ep.out) + (size_t)m * ep.ldo + n) =
+        make_float4(old.x + (v.x + bb[0]), old.y + (v.y + bb[1]), old.z + (v.z + bb[2]),
+                    old.w + (v.w + bb[3]));
+    return;
+  }
+  const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const EpiCol<OutT, EPI> col(ep, n + c);
