@@ -391,20 +391,31 @@ orca_status orca_iteration(orca_ctx* c, const orca_req_desc* reqs, int32_t n_req
   const size_t gpb = c->gpart_bytes;
 
   HIP_TRY(launch_to_f32(dt, x, resid, int64_t(R) * H, s), "input conversion");
+  // LN1 of layer 0 here; every later LayerNorm runs with the residual
+  // Linear before it (one kernel with its split-K reduce when that applies)
+  HIP_TRY(launch_layernorm(dt, resid, c->layers[0].ln1_g, c->layers[0].ln1_b, a, R, H, d.ln_eps, s),
+          "LN1");
   for (int l = 0; l < d.layers; ++l) {
     const orca_layer_weights& w = c->layers[l];
     QkvDest qd{q, static_cast<char*>(c->k_pool) + pool * l, static_cast<char*>(c->v_pool) + pool * l,
                row_dst, H, H / d.heads, d.kv_capacity};
-    HIP_TRY(launch_layernorm(dt, resid, w.ln1_g, w.ln1_b, a, R, H, d.ln_eps, s), "LN1");
     HIP_TRY(launch_linear(dt, EPI_QKV, a, w.w_qkv, w.b_qkv, nullptr, &qd, R, 3 * H, H, gp, gpb, s), "QKV");
     st = run_attention(c, l, aa, q, o, s);
     if (st != ORCA_OK) return st;
-    HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_RESID, o, w.w_o, w.b_o, resid, nullptr, R, H, H, gp, gpb, s),
-            "output projection");
-    HIP_TRY(launch_layernorm(dt, resid, w.ln2_g, w.ln2_b, a, R, H, d.ln_eps, s), "LN2");
+    HIP_TRY(launch_linear_resid_ln(dt, o, w.w_o, w.b_o, resid, R, H, H, gp, gpb, w.ln2_g, w.ln2_b, a,
+                                   d.ln_eps, s),
+            "output projection + LN2");
     HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_GELU, a, w.w_1, w.b_1, f, nullptr, R, F, H, gp, gpb, s), "FFN1");
-    HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_RESID, f, w.w_2, w.b_2, resid, nullptr, R, H, F, gp, gpb, s),
-            "FFN2");
+    if (l + 1 < d.layers) {
+      const orca_layer_weights& wn = c->layers[l + 1];
+      HIP_TRY(launch_linear_resid_ln(dt, f, w.w_2, w.b_2, resid, R, H, F, gp, gpb, wn.ln1_g, wn.ln1_b,
+                                     a, d.ln_eps, s),
+              "FFN2 + next LN1");
+    } else {
+      HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_RESID, f, w.w_2, w.b_2, resid, nullptr, R, H, F, gp, gpb,
+                            s),
+              "FFN2");
+    }
   }
   HIP_TRY(launch_from_f32(dt, resid, y, int64_t(R) * H, s), "output conversion");
   return ORCA_OK;

@@ -782,9 +782,9 @@ static void launch_partial(const SplitPlan& p, const void* a, const void* w, con
                                                                 p.splits, p.kt_per_split);
 }
 
-template <int EPI>
-static void launch_split(const SplitPlan& p, const void* a, const void* w, const void* bias,
-                         const EpiParams& ep, float* part, int m, int n, int k, hipStream_t s) {
+// the partial-sum GEMM of a split plan: fp32 planes part[splits][m][n]
+static void launch_partials(const SplitPlan& p, const void* a, const void* w, float* part, int m,
+                            int n, int k, hipStream_t s) {
   EpiParams pp{};
   pp.out = part;
   pp.ldo = n;
@@ -793,6 +793,12 @@ static void launch_split(const SplitPlan& p, const void* a, const void* w, const
   else if (p.tile == 1) launch_partial<1, 4, 2, 1, true>(p, a, w, pp, m, n, k, s);
   else if (p.tile == 2) launch_partial<2, 2, 2, 2>(p, a, w, pp, m, n, k, s);
   else launch_partial<4, 2, 2, 4>(p, a, w, pp, m, n, k, s);
+}
+
+template <int EPI>
+static void launch_split(const SplitPlan& p, const void* a, const void* w, const void* bias,
+                         const EpiParams& ep, float* part, int m, int n, int k, hipStream_t s) {
+  launch_partials(p, a, w, part, m, n, k, s);
   const int threads = m * (n / 4);
   hipLaunchKernelGGL(skinny_reduce_kernel<EPI>, dim3((threads + 255) / 256), dim3(256), 0, s,
                      part, p.splits, (const bf16*)bias, ep, m, n);
@@ -865,6 +871,38 @@ hipError_t launch_linear(int dtype, int epilogue, const void* a, const void* w, 
     default: launch_typed<EPI_QKV>(dtype, a, w, bias, ep, ws, ws_bytes, m, n, k, s); break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_linear_resid_ln(int dtype, const void* a, const void* w, const void* bias,
+                                  float* resid, int m, int n, int k, void* ws, size_t ws_bytes,
+                                  const void* ln_g, const void* ln_b, void* ln_out, float eps,
+                                  hipStream_t s) {
+  if (m == 0) return hipSuccess;
+  SplitPlan sp{};
+  if (dtype == ORCA_BF16 && plan_gemm(m, n, k, sp) == 10 && ws &&
+      ws_bytes >= (size_t)sp.splits * m * n * sizeof(float)) {
+    float* part = static_cast<float*>(ws);
+    launch_partials(sp, a, w, part, m, n, k, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const hipError_t f =
+        launch_reduce_resid_ln(part, sp.splits, bias, resid, m, n, ln_g, ln_b, ln_out, eps, s);
+    if (f != hipErrorNotSupported) return f;
+    // row too wide for the fused kernel: the separate reduce, then the LN
+    EpiParams ep{};
+    ep.out = resid;
+    ep.ldo = n;
+    const int threads = m * (n / 4);
+    hipLaunchKernelGGL(skinny_reduce_kernel<ORCA_EPI_BIAS_RESID>, dim3((threads + 255) / 256),
+                       dim3(256), 0, s, part, sp.splits, (const bf16*)bias, ep, m, n);
+  } else {
+    const hipError_t e = launch_linear(dtype, ORCA_EPI_BIAS_RESID, a, w, bias, resid, nullptr, m,
+                                       n, k, ws, ws_bytes, s);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_layernorm(dtype, resid, ln_g, ln_b, ln_out, m, n, eps, s);
 }
 
 }  // namespace orca

@@ -10,6 +10,11 @@ namespace orca {
 // ---- LayerNorm and conversions (ln.hip) ----------------------------------
 hipError_t launch_layernorm(int dtype, const float* x, const void* g, const void* b, void* out,
                             int rows, int hidden, float eps, hipStream_t s);
+// bf16 only: resid[r] += sum of the `splits` fp32 planes part[s][r] + bias,
+// then out[r] = LN(resid[r]); hipErrorNotSupported past hidden = 12288
+hipError_t launch_reduce_resid_ln(const float* part, int splits, const void* bias, float* resid,
+                                  int rows, int hidden, const void* g, const void* b, void* out,
+                                  float eps, hipStream_t s);
 hipError_t launch_to_f32(int dtype, const void* in, float* out, int64_t n, hipStream_t s);
 hipError_t launch_from_f32(int dtype, const float* in, void* out, int64_t n, hipStream_t s);
 
@@ -39,6 +44,13 @@ size_t linear_workspace_bytes(int dtype, int m, int n, int k);
 hipError_t launch_linear(int dtype, int epilogue, const void* a, const void* w, const void* bias,
                          void* out, const QkvDest* qkv, int m, int n, int k, void* ws,
                          size_t ws_bytes, hipStream_t s);
+// The residual-epilogue Linear (out is the fp32 residual [m][n]) followed
+// by the LayerNorm of the new residual into ln_out; on the split-K path the
+// two share one kernel after the partial GEMM.
+hipError_t launch_linear_resid_ln(int dtype, const void* a, const void* w, const void* bias,
+                                  float* resid, int m, int n, int k, void* ws, size_t ws_bytes,
+                                  const void* ln_g, const void* ln_b, void* ln_out, float eps,
+                                  hipStream_t s);
 
 // ---- Attention (attn.hip) --------------------------------------------------
 // Device request record: same layout as orca_req_desc.

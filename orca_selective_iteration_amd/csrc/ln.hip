@@ -97,6 +97,88 @@ __global__ __launch_bounds__(NT) void layernorm_kernel(const float* __restrict__
   }
 }
 
+// Few-rows Linear with the residual epilogue, fused with the LayerNorm that
+// follows it: one workgroup per row adds the row's fp32 split-K partial
+// planes (in plane order) and the bias to the residual, exactly as the
+// split-K reduce does, writes the new residual, and normalises it.  Saves
+// the separate reduce launch (a tiny kernel costs ~4-5 us whatever it does).
+// NT threads with NV float4 chunks each cover the row; every load of a
+// chunk is issued before its first use.
+template <int NT, int NV>
+__global__ __launch_bounds__(NT) void reduce_resid_ln_kernel(
+    const float* __restrict__ part, int splits, const bf16* __restrict__ bias,
+    float* __restrict__ resid, int rows, int hidden, const bf16* __restrict__ g,
+    const bf16* __restrict__ b, bf16* __restrict__ out, float eps) {
+  __shared__ float red[NT / 64];
+  const int row = blockIdx.x;
+  const int nv = hidden / 4;
+  const size_t plane = (size_t)rows * hidden, rbase = (size_t)row * hidden;
+  float4 x[NV], v[NV], bi[NV], gg[NV], bb[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = min((int)threadIdx.x + i * NT, nv - 1);
+    x[i] = *reinterpret_cast<const float4*>(resid + rbase + c * 4);
+    v[i] = *reinterpret_cast<const float4*>(part + rbase + c * 4);
+    bi[i] = load4(bias + c * 4);
+    gg[i] = load4(g + c * 4);
+    bb[i] = load4(b + c * 4);
+  }
+  for (int s0 = 1; s0 < splits; s0 += 4) {
+    float4 t[4][NV];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c = min((int)threadIdx.x + i * NT, nv - 1);
+        t[u][i] = *reinterpret_cast<const float4*>(part + min(s0 + u, splits - 1) * plane +
+                                                   rbase + c * 4);
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool on = s0 + u < splits;   // a select: behind a branch the load sinks into it
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        v[i].x += on ? t[u][i].x : 0.f; v[i].y += on ? t[u][i].y : 0.f;
+        v[i].z += on ? t[u][i].z : 0.f; v[i].w += on ? t[u][i].w : 0.f;
+      }
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = threadIdx.x + i * NT;
+    x[i] = make_float4(x[i].x + (v[i].x + bi[i].x), x[i].y + (v[i].y + bi[i].y),
+                       x[i].z + (v[i].z + bi[i].z), x[i].w + (v[i].w + bi[i].w));
+    if (c < nv) {
+      *reinterpret_cast<float4*>(resid + rbase + c * 4) = x[i];
+      s += (x[i].x + x[i].y) + (x[i].z + x[i].w);
+    }
+  }
+  const float mean = block_sum<NT>(s, red) / hidden;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = threadIdx.x + i * NT;
+    if (c < nv) {
+      const float a = x[i].x - mean, e = x[i].y - mean, cc = x[i].z - mean, d = x[i].w - mean;
+      q += (a * a + e * e) + (cc * cc + d * d);
+    }
+  }
+  const float rstd = rsqrtf(block_sum<NT>(q, red) / hidden + eps);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = threadIdx.x + i * NT;
+    if (c < nv) {
+      float4 y;
+      y.x = (x[i].x - mean) * rstd * gg[i].x + bb[i].x;
+      y.y = (x[i].y - mean) * rstd * gg[i].y + bb[i].y;
+      y.z = (x[i].z - mean) * rstd * gg[i].z + bb[i].z;
+      y.w = (x[i].w - mean) * rstd * gg[i].w + bb[i].w;
+      store4(out + rbase + c * 4, y);
+    }
+  }
+}
+
 template <typename T>
 __global__ void to_f32_kernel(const T* __restrict__ in, float* __restrict__ out, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
@@ -142,6 +224,27 @@ static dim3 grid_for(int64_t n) {
   int64_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   return dim3((unsigned)(blocks > 0 ? blocks : 1));
+}
+
+hipError_t launch_reduce_resid_ln(const float* part, int splits, const void* bias, float* resid,
+                                  int rows, int hidden, const void* g, const void* b, void* out,
+                                  float eps, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int v4 = hidden / 4;
+  if (hidden % 4 != 0 || splits < 1) return hipErrorNotSupported;
+#define ORCA_RRLN(NT, NV)                                                                     \
+  hipLaunchKernelGGL((reduce_resid_ln_kernel<NT, NV>), dim3(rows), dim3(NT), 0, s, part, splits, \
+                     (const bf16*)bias, resid, rows, hidden, (const bf16*)g, (const bf16*)b,  \
+                     (bf16*)out, eps)
+  if (v4 <= 256 * 2) ORCA_RRLN(256, 2);
+  else if (v4 <= 512 * 2) ORCA_RRLN(512, 2);
+  else if (v4 <= 640 * 2) ORCA_RRLN(640, 2);
+  else if (v4 <= 768 * 2) ORCA_RRLN(768, 2);
+  else if (v4 <= 1024 * 2) ORCA_RRLN(1024, 2);
+  else if (v4 <= 768 * 4) ORCA_RRLN(768, 4);
+  else return hipErrorNotSupported;   // (1024 x 4 would spill registers)
+#undef ORCA_RRLN
+  return hipGetLastError();
 }
 
 hipError_t launch_to_f32(int dtype, const void* in, float* out, int64_t n, hipStream_t s) {
