@@ -12,6 +12,8 @@ checked exactly:
     whole batch from seeded input rows; the oracle checks the complete first
     initiation prompt (or its first rows, whose causal attention needs no
     later row) and sampled increment requests.
+The decode batch (64 increment rows, no prompt) runs every Linear on the
+split-K path, with the residual reduces fused into the LayerNorms.
 These need ~160 GB of device memory and minutes of host time: marked `big`.
 """
 import numpy as np
@@ -100,10 +102,11 @@ def run_fullsize(name, n_full_depth, init_rows, layers_checked, seed=0):
             finally:
                 L.orca_destroy(ctx)
             p = layer64(model, l)
-            i0 = init[0]
-            n0 = min(work.q_len[i0], init_rows)
-            picks = [(i0, n0)] + [(i, 1) for i in
-                                  sorted(rng.choice(incr, size=8, replace=False).tolist())]
+            picks = [(i, 1) for i in sorted(rng.choice(incr, size=8, replace=False).tolist())]
+            if init:
+                i0 = init[0]
+                n0 = min(work.q_len[i0], init_rows)
+                picks = [(i0, n0)] + picks
             for i, n in picks:
                 kv = work.kv_len[i]
                 kc = cache64(model, l, i, 0, kv)
@@ -114,8 +117,8 @@ def run_fullsize(name, n_full_depth, init_rows, layers_checked, seed=0):
                 errs = (rel_err(host64(yl[offs[i]:offs[i] + n]), yr), rel_err(gk, app[0][0]),
                         rel_err(gv, app[0][1]))
                 assert max(errs) < TOL["bf16"], (l, i, n, errs)
-            print(f"  layer {l}: initiation rows 0..{n0 - 1} of request {i0} and 8 increments"
-                  f" ok", flush=True)
+            print(f"  layer {l}: " + (f"initiation rows 0..{n0 - 1} of request {i0} and "
+                                       if init else "") + "8 increments ok", flush=True)
             del p
     finally:
         model.close()
@@ -131,3 +134,8 @@ def test_gpt13b_40_layers_full_size():
 @pytest.mark.timeout(900)
 def test_gpt175b_layer_shape_8_layers_full_size():
     run_fullsize("gpt175b-8l", n_full_depth=2, init_rows=384, layers_checked=[0, 7])
+
+
+@pytest.mark.timeout(900)
+def test_gpt13b_decode_batch_40_layers_full_size():
+    run_fullsize("gpt13b-40l-decode64", n_full_depth=3, init_rows=0, layers_checked=[0, 39])
