@@ -192,3 +192,17 @@ def test_empty_batch_and_invalid_descriptors():
         assert bool((y == 9.0).all())
     finally:
         model.close()
+
+
+@pytest.mark.big
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("layers,hidden,heads", [(2, 8192, 64), (1, 10240, 80)])
+def test_wide_rows_on_the_split_path(layers, hidden, heads):
+    """Few rows of wide models: every Linear on the split-K path, the
+    residual reduces fused with the LayerNorms at their widest row
+    configurations (1024 threads x 2 and 768 x 4 float4 per row)."""
+    print(f"case wide split path layers={layers} hidden={hidden}", flush=True)
+    work = synth.custom_workload(layers, hidden, heads, 4 * hidden, "bf16",
+                                 [1] * 12 + [5], [30] * 6 + [200] * 6 + [0])
+    _, m = check_against_oracle(work, seed=hidden)
+    m.close()
