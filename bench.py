@@ -316,7 +316,7 @@ def main():
     decode = None
     incr = [i for i in range(work.n_reqs) if work.kv_len[i] > 0]
     if args.only in (None, "decode") and incr:
-        d_reqs = model.descriptors(reqs=incr)
+        d_reqs = L.req_array(model.descriptors(reqs=incr))
         n = len(incr)
         q = synth.device_normal_(torch.empty((n, H), dtype=model.tdt, device="cuda"), 13)
         o = torch.empty_like(q)

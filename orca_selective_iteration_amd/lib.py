@@ -141,7 +141,10 @@ def stream_handle(stream) -> Optional[int]:
 
 def req_array(reqs: Sequence) -> "ctypes.Array":
     """Descriptors from tuples (q_offset, q_len, kv_len, phase, kv_base) or
-    orca_req_desc instances."""
+    orca_req_desc instances; an array this function built passes through
+    (callers timing short launches marshal once)."""
+    if isinstance(reqs, ctypes.Array) and reqs._type_ is orca_req_desc:
+        return reqs
     arr = (orca_req_desc * max(len(reqs), 1))()
     for i, r in enumerate(reqs):
         arr[i] = r if isinstance(r, orca_req_desc) else orca_req_desc(*[int(v) for v in r])
