@@ -240,3 +240,19 @@ def test_op_validation_fails_before_gpu():
     with pytest.raises(L.OrcaError) as e:
         L.orca_op_qkv(L.ORCA_BF16, 16, 16, 16, 16, 16, 16, 16, 4, 256, 8, 100)
     assert e.value.status == L.ORCA_ERR_UNSUPPORTED          # head dim 32 in bf16
+
+
+# the launch planner's split-K choice, seen through the workspace it asks for
+# (split-K planes are fp32 [splits][m][n]; 0 bytes means a tiled launch)
+@pytest.mark.parametrize("m,n,k,splits", [
+    (64, 15360, 5120, 2),    # 13B QKV at 64 rows: 120 column tiles, one round at 2 splits
+    (64, 5120, 5120, 6),     # output projection: 40 tiles x 6 splits = 240 workgroups
+    (64, 20480, 5120, 3),    # FFN1: 160 tiles; 3 splits beat 2 (imbalanced) and 4 (two rounds)
+    (64, 5120, 20480, 6),    # FFN2
+    (16, 15360, 5120, 2),
+    (2176, 20480, 5120, 0),  # the 13B mixed batch: tiles fill the GPU, no split
+    (4096, 5120, 5120, 0),
+])
+def test_planner_split_counts(m, n, k, splits):
+    assert L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k) == splits * m * n * 4
+    assert L.orca_op_linear_workspace_bytes(L.ORCA_F32, m, n, k) == 0
