@@ -263,6 +263,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   typedef uint32_t Stage __attribute__((ext_vector_type(4 * NL)));
   Stage kreg, vreg;
   const int vkey = tid & 63;
+  // byte selectors of v_perm_b32 (bytes 0-3: second operand, 4-7: first):
+  // even key lanes take (own.lo16, neighbour.lo16), odd ones
+  // (neighbour.hi16, own.hi16)
+  const uint32_t vsel = (vkey & 1) ? 0x03020706u : 0x05040100u;
 #define ORCA_PF_LOAD(K0)                                                                     \
   _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                           \
     const int c = tid + 256 * i, key = c / (D / 8), ch = c % (D / 8);                        \
@@ -284,13 +288,15 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
       const int vch = (tid >> 6) + 4 * i;
       // V^T: this lane holds dims d, d+1 of key vkey in each word; with the
       // neighbouring key's word (lane ^ 1, a DPP move) an even lane writes
-      // row d and an odd lane row d+1, two consecutive keys per 32-bit store
+      // row d (its own low half, then the neighbour's) and an odd lane row
+      // d+1 (the neighbour's high half, then its own), two consecutive keys
+      // per 32-bit store; one byte permute with a per-lane selector (a
+      // select between the two forms compiled to a divergent branch)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t wv = vreg[4 * i + j];
         const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wv, 0xB1, 0xF, 0xF, false);
-        const uint32_t word = (vkey & 1) ? ((nb >> 16) | (wv & 0xffff0000u))
-                                         : ((wv & 0xffffu) | (nb << 16));
+        const uint32_t word = __builtin_amdgcn_perm(nb, wv, vsel);
         *reinterpret_cast<uint32_t*>(&sV[(vch * 8 + 2 * j + (vkey & 1)) * VLD + (vkey & ~1)]) = word;
       }
     }
