@@ -214,10 +214,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   constexpr int OLD = D + 8;             // output staging row stride
   constexpr int KV_ELEMS = BKV * KLD + D * VLD;
   constexpr int O_ELEMS = BQ * OLD;
-  constexpr int SMEM = KV_ELEMS > O_ELEMS ? KV_ELEMS : O_ELEMS;
+  // two K/V stages (the next step is written while this one is read)
+  constexpr int SMEM = 2 * KV_ELEMS > O_ELEMS ? 2 * KV_ELEMS : O_ELEMS;
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
-  uint16_t* sK = smem;
-  uint16_t* sV = smem + BKV * KLD;
 
   // grid (heads, items): all heads of the first (longest) item go first
   const PrefillItem it = a.pf[blockIdx.y];
@@ -277,32 +276,45 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     kreg[4 * i] = tk.x; kreg[4 * i + 1] = tk.y; kreg[4 * i + 2] = tk.z; kreg[4 * i + 3] = tk.w; \
     vreg[4 * i] = tv.x; vreg[4 * i + 1] = tv.y; vreg[4 * i + 2] = tv.z; vreg[4 * i + 3] = tv.w; \
   }
+  // V^T: this lane holds dims d, d+1 of key vkey in each word; with the
+  // neighbouring key's word (lane ^ 1, a DPP move) an even lane writes row d
+  // (its own low half, then the neighbour's) and an odd lane row d+1 (the
+  // neighbour's high half, then its own), two consecutive keys per 32-bit
+  // store: one byte permute with a per-lane selector (a select between the
+  // two forms compiled to a divergent branch)
+#define ORCA_PF_STORE(BUF)                                                                   \
+  {                                                                                          \
+    uint16_t* const stK = smem + (BUF) * KV_ELEMS;                                           \
+    uint16_t* const stV = stK + BKV * KLD;                                                   \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                         \
+      const int c = tid + 256 * i, key = c / (D / 8), ch = c % (D / 8);                      \
+      *reinterpret_cast<uint4*>(&stK[key * KLD + ch * 8]) =                                  \
+          make_uint4(kreg[4 * i], kreg[4 * i + 1], kreg[4 * i + 2], kreg[4 * i + 3]);        \
+      const int vch = (tid >> 6) + 4 * i;                                                    \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                        \
+        const uint32_t wv = vreg[4 * i + j];                                                 \
+        const uint32_t nb =                                                                  \
+            (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wv, 0xB1, 0xF, 0xF, false);       \
+        *reinterpret_cast<uint32_t*>(&stV[(vch * 8 + 2 * j + (vkey & 1)) * VLD + (vkey & ~1)]) = \
+            __builtin_amdgcn_perm(nb, wv, vsel);                                             \
+      }                                                                                      \
+    }                                                                                        \
+  }
   ORCA_PF_LOAD(0)
-  for (int k0 = 0; k0 < kend; k0 += BKV) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int c = tid + 256 * i, key = c / (D / 8), ch = c % (D / 8);
-      *reinterpret_cast<uint4*>(&sK[key * KLD + ch * 8]) =
-          make_uint4(kreg[4 * i], kreg[4 * i + 1], kreg[4 * i + 2], kreg[4 * i + 3]);
-      const int vch = (tid >> 6) + 4 * i;
-      // V^T: this lane holds dims d, d+1 of key vkey in each word; with the
-      // neighbouring key's word (lane ^ 1, a DPP move) an even lane writes
-      // row d (its own low half, then the neighbour's) and an odd lane row
-      // d+1 (the neighbour's high half, then its own), two consecutive keys
-      // per 32-bit store; one byte permute with a per-lane selector (a
-      // select between the two forms compiled to a divergent branch)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t wv = vreg[4 * i + j];
-        const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wv, 0xB1, 0xF, 0xF, false);
-        const uint32_t word = __builtin_amdgcn_perm(nb, wv, vsel);
-        *reinterpret_cast<uint32_t*>(&sV[(vch * 8 + 2 * j + (vkey & 1)) * VLD + (vkey & ~1)]) = word;
-      }
+  ORCA_PF_STORE(0)
+  ORCA_PF_LOAD(BKV)
+  __syncthreads();
+  int cur = 0;
+  for (int k0 = 0; k0 < kend; k0 += BKV, cur ^= 1) {
+    // step k+1's K/V into the other stage: it was last read in step k-1,
+    // which the barrier closing that step has ended for every wave
+    if (k0 + BKV < kend) {
+      ORCA_PF_STORE(cur ^ 1)
     }
-    __syncthreads();
-    ORCA_PF_LOAD(k0 + BKV)
-    if (k0 >= kend_wave) continue;
+    ORCA_PF_LOAD(k0 + 2 * BKV)
+    if (k0 < kend_wave) {
+    const uint16_t* sK = smem + cur * KV_ELEMS;
+    const uint16_t* sV = sK + BKV * KLD;
 
     // S^T = K Q^T for keys k0 .. k0+63 (two 32-key tiles)
     f32x16_t s[2];
@@ -384,9 +396,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
         o[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[dm], 0, 0, 0);
       }
     }
+    }
+    __syncthreads();
   }
 
 #undef ORCA_PF_LOAD
+#undef ORCA_PF_STORE
   // normalise, transpose through LDS, write the rows
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
