@@ -384,7 +384,7 @@ void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
 // twelve waves meet at one barrier per K step: after it the MFMA waves read
 // the buffer written before it, while the loaders fill the other one.
 // Needs an even number of K steps and element offsets below 2^31.
-constexpr int WS_THREADS = 768, WS_LOADERS = 256, WS_MIN_K = 8192;
+constexpr int WS_THREADS = 768, WS_LOADERS = 256;
 
 template <int EPI>
 __global__ __launch_bounds__(WS_THREADS, 1)
@@ -498,6 +498,165 @@ void gemm_ws_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
   // and pool-slot reads spill
   store_wave_tile<EPI, TI, TJ, 0>(acc, bias, ep, M, N, tm * BM + wm * 32 * TI,
                                   tn * BN + wn * 32 * TJ, lane);
+}
+
+// ------------------------------------------- one wave per SIMD, 256 x 256/192
+
+// 256 x (64 TJ) tile on four waves (2 x 2, each 128 x 32 TJ as 4 x TJ
+// accumulators, held in the accumulation registers): one wave per SIMD, so
+// the latency is hidden inside each wave rather than by a second wave.  The
+// fragments of sub-step ks+1 are read from LDS while the MFMAs of sub-step
+// ks run; the global loads run two K steps ahead; and the one barrier of a
+// K step sits before its last sub-step's MFMAs, so the next step's first
+// fragment reads overlap them.  Needs an even number of K steps and element
+// offsets below 2^31.
+constexpr int W4_THREADS = 256;
+
+template <int EPI, int TJ>
+__global__ __launch_bounds__(W4_THREADS, 1)
+void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
+                    const bf16* __restrict__ bias, EpiParams ep, int M, int N, int K,
+                    int tiles_m) {
+  constexpr int TI = 4, BM = 256, BN = 64 * TJ;
+  // 16-byte chunks per lane and K step: LA of A rows, then LB of W rows
+  constexpr int LA = BM * 8 / W4_THREADS, LB = BN * 8 / W4_THREADS, NC = LA + LB;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDK];
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int tm = logical % tiles_m, tn = logical / tiles_m;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int KT = K / BK;
+
+  // loads: lane tid moves chunk tid % 8 of rows tid / 8 + 32 i; byte
+  // offsets from a uniform base keep each address to one register
+  const int ch = tid & 7;
+  uint32_t offA[LA], offB[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i)
+    offA[i] = (uint32_t)(min(tm * BM + (tid >> 3) + 32 * i, M - 1) * K + ch * 8) * 2u;
+#pragma unroll
+  for (int i = 0; i < LB; ++i)
+    offB[i] = (uint32_t)(min(tn * BN + (tid >> 3) + 32 * i, N - 1) * K + ch * 8) * 2u;
+  const int oL = (tid >> 3) * LDK + ch * 8;   // chunk i lands 32 rows further down
+  typedef uint32_t Stage __attribute__((ext_vector_type(4 * NC)));
+  typedef uint32_t U4 __attribute__((ext_vector_type(4)));
+  Stage s0, s1;
+  // buffer loads: a 32-bit lane offset plus the K step's offset in a scalar
+  // register, so no 64-bit address is formed per load
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)A, (short)0, (int)(uint32_t)std::min<size_t>((size_t)M * K * 2, 0xffffffffu),
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)W, (short)0, (int)(uint32_t)std::min<size_t>((size_t)N * K * 2, 0xffffffffu),
+      0x00020000);
+// chunk c of a stage: c < LA are A rows, the rest W rows
+#define ORCA_W4_LOAD(S, KS, C0, C1)                                                           \
+  {                                                                                           \
+    const int kb = (KS) * BK * 2;                                                             \
+    _Pragma("unroll") for (int c = (C0); c < (C1); ++c) {                                     \
+      const U4 t = c < LA ? __builtin_amdgcn_raw_buffer_load_b128(rA, offA[c], kb, 0)         \
+                          : __builtin_amdgcn_raw_buffer_load_b128(rB, offB[c - LA], kb, 0);   \
+      S[4 * c] = t.x; S[4 * c + 1] = t.y; S[4 * c + 2] = t.z; S[4 * c + 3] = t.w;             \
+    }                                                                                         \
+  }
+#define ORCA_W4_STORE(S, BUF, C0, C1)                                                         \
+  {                                                                                           \
+    _Pragma("unroll") for (int c = (C0); c < (C1); ++c)                                       \
+        *reinterpret_cast<uint4*>(c < LA ? &sA[BUF][oL + c * 32 * LDK]                        \
+                                         : &sB[BUF][oL + (c - LA) * 32 * LDK]) =              \
+            make_uint4(S[4 * c], S[4 * c + 1], S[4 * c + 2], S[4 * c + 3]);                   \
+  }
+
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  const int a_off = (wm * 32 * TI + fr) * LDK + fk, b_off = (wn * 32 * TJ + fr) * LDK + fk;
+  f32x16_t acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  bf16x8_t fa0[TI], fb0[TJ], fa1[TI], fb1[TJ];
+#define ORCA_W4_FRAGS(FA, FB, BUF, KS)                                                        \
+  _Pragma("unroll") for (int i = 0; i < TI; ++i) FA[i] =                                      \
+      *reinterpret_cast<const bf16x8_t*>(&sA[BUF][a_off + i * 32 * LDK + (KS) * 16]);         \
+  _Pragma("unroll") for (int j = 0; j < TJ; ++j) FB[j] =                                      \
+      *reinterpret_cast<const bf16x8_t*>(&sB[BUF][b_off + j * 32 * LDK + (KS) * 16]);
+#define ORCA_W4_MFMA(FA, FB)                                                                  \
+  _Pragma("unroll") for (int i = 0; i < TI; ++i)                                              \
+      _Pragma("unroll") for (int j = 0; j < TJ; ++j) acc[i][j] =                              \
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0);
+  // step kt (LDS buffer CUR): loads of step kt+2 into LS, step kt+1 from SS
+  // into the other buffer, then the four sub-steps with the barrier before
+  // the last one's MFMAs
+  // sched_group_barrier masks: MFMA 0x8, VMEM read 0x20, DS read 0x100,
+  // DS write 0x200.  A K step is four phases of NM = 4 TJ MFMAs (one
+  // sub-step each), fenced by scheduling barriers.  The step's NC global
+  // loads (of step kt+2), NC LDS writes (of step kt+1, into the other
+  // buffer) and the fragment reads are spread evenly over them, so neither
+  // the LDS nor the address path sees a burst: each phase reads the next
+  // sub-step's fragments and issues a quarter of the loads; phases a-c
+  // write a third of the chunks each.  The barrier sits between phases c
+  // and d: phase d's fragment reads are of the next K step's first sub-step.
+  constexpr int NM = TI * TJ, NR = TI + TJ;
+  constexpr int G1 = NC / 4, G2 = NC / 2, G3 = 3 * NC / 4, W1 = NC / 3, W2 = 2 * NC / 3;
+#define ORCA_W4_SPREAD(NG, NW)                                                                \
+  _Pragma("unroll") for (int j = 0; j < NM; ++j) {                                            \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                        \
+    if (j < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            \
+    if (((j + 1) * (NG)) / NM > (j * (NG)) / NM)                                              \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                      \
+    if (((j + 1) * (NW)) / NM > (j * (NW)) / NM)                                              \
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                                      \
+  }
+#define ORCA_W4_STEP(CUR, LS, SS)                                                             \
+  {                                                                                           \
+    const int kl = min(kt + (CUR) + 2, KT - 1);                                               \
+    ORCA_W4_FRAGS(fa1, fb1, CUR, 1)                                                           \
+    ORCA_W4_LOAD(LS, kl, 0, G1)                                                               \
+    ORCA_W4_STORE(SS, (CUR) ^ 1, 0, W1)                                                       \
+    ORCA_W4_MFMA(fa0, fb0)                                                                    \
+    ORCA_W4_SPREAD(G1, W1)                                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    ORCA_W4_FRAGS(fa0, fb0, CUR, 2)                                                           \
+    ORCA_W4_LOAD(LS, kl, G1, G2)                                                              \
+    ORCA_W4_STORE(SS, (CUR) ^ 1, W1, W2)                                                      \
+    ORCA_W4_MFMA(fa1, fb1)                                                                    \
+    ORCA_W4_SPREAD(G2 - G1, W2 - W1)                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    ORCA_W4_FRAGS(fa1, fb1, CUR, 3)                                                           \
+    ORCA_W4_LOAD(LS, kl, G2, G3)                                                              \
+    ORCA_W4_STORE(SS, (CUR) ^ 1, W2, NC)                                                      \
+    ORCA_W4_MFMA(fa0, fb0)                                                                    \
+    ORCA_W4_SPREAD(G3 - G2, NC - W2)                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    __syncthreads();                                                                          \
+    ORCA_W4_FRAGS(fa0, fb0, (CUR) ^ 1, 0)                                                     \
+    ORCA_W4_LOAD(LS, kl, G3, NC)                                                              \
+    ORCA_W4_MFMA(fa1, fb1)                                                                    \
+    ORCA_W4_SPREAD(NC - G3, 0)                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+  }
+  ORCA_W4_LOAD(s0, 0, 0, NC)
+  ORCA_W4_LOAD(s1, min(1, KT - 1), 0, NC)
+  ORCA_W4_STORE(s0, 0, 0, NC)
+  __syncthreads();
+  ORCA_W4_FRAGS(fa0, fb0, 0, 0)
+  for (int kt = 0; kt < KT; kt += 2) {
+    ORCA_W4_STEP(0, s0, s1)
+    ORCA_W4_STEP(1, s1, s0)
+  }
+#undef ORCA_W4_STEP
+#undef ORCA_W4_SPREAD
+#undef ORCA_W4_MFMA
+#undef ORCA_W4_FRAGS
+#undef ORCA_W4_LOAD
+#undef ORCA_W4_STORE
+  store_wave_tile<EPI, TI, TJ>(acc, bias, ep, M, N, tm * BM + wm * 32 * TI,
+                               tn * BN + wn * 32 * TJ, lane);
 }
 
 // ---------------------------------------------------------------- few rows
@@ -618,8 +777,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 //   7: as 0, with two K steps of global loads in flight
 //   8: 4x2 waves, 2x3 tiles -> 256 x 192, 512 threads, two K steps in flight
 //  10: split-K (see plan_gemm)
+//  11: wave-specialised 256 x 256 (eight MFMA waves, four loader waves)
+//  12: four waves, 4x4 tiles each -> 256 x 256, one wave per SIMD
+//  13: four waves, 4x3 tiles each -> 256 x 192, one wave per SIMD
 // (6, 7 and 8 need an even number of K steps and fall back to 3, 0 and the
-// one-step 256 x 192 form.)
+// one-step 256 x 192 form; 11, 12 and 13 need an even number of K steps and
+// element offsets below 2^31 and fall back to 6, 6 and 8.  The planner
+// picks among 12, 13, 7 and 10; the others stay for tests and sweeps.)
 template <int EPI, int WGM, int WGN, int TI, int TJ, bool PIPE = false, bool STREAM_W = false>
 static void launch_mfma(const void* a, const void* w, const void* bias, const EpiParams& ep, int m,
                         int n, int k, hipStream_t s, int splits = 1, int kt_per_split = 0) {
@@ -691,25 +855,25 @@ static bool few_rows_plan(int m, int n, int k, SplitPlan& p) {
 
 // Estimated time of the tiled launches, in units of one 256 x 256 tile-round
 // per unit of K: rounds of resident workgroups times the output area a CU
-// covers per round, over the tile's measured rate relative to 256 x 256
-// (MI355X, 13B layer shapes, K steps even: 256 x 192 at 0.945, 128 x 128
-// at 0.84).  The last round counts whole: a launch that leaves CUs idle in
-// it pays for them.
+// covers per round, over the tile's measured rate relative to the 256 x 256
+// four-wave kernel (MI355X, 13B and 175B layer shapes: its 256 x 192 form
+// at 0.92, the 128 x 128 eight-wave tile at 0.76).  The last round counts
+// whole: a launch that leaves CUs idle in it pays for them.
 static double cost_tiled(int v, int m, int n) {
   switch (v) {
-    case 6: return ceil_div_l(ceil_div_l(m, 256) * ceil_div_l(n, 256), NUM_CU) * 65536.0;
-    case 8: return ceil_div_l(ceil_div_l(m, 256) * ceil_div_l(n, 192), NUM_CU) * 49152.0 / 0.945;
-    default: return ceil_div_l(ceil_div_l(m, 128) * ceil_div_l(n, 128), 2 * NUM_CU) * 32768.0 / 0.84;
+    case 12: return ceil_div_l(ceil_div_l(m, 256) * ceil_div_l(n, 256), NUM_CU) * 65536.0;
+    case 13: return ceil_div_l(ceil_div_l(m, 256) * ceil_div_l(n, 192), NUM_CU) * 49152.0 / 0.92;
+    default: return ceil_div_l(ceil_div_l(m, 128) * ceil_div_l(n, 128), 2 * NUM_CU) * 32768.0 / 0.76;
   }
 }
 // The tiled variant of least estimated cost; another tile than 256 x 256
-// only on a predicted gain of 3% or more (the model is coarse; in a full
-// iteration the 175B shapes, where 256 x 192 was predicted 1% faster, ran 1%
-// slower).
+// only on a predicted gain of 3% or more (the model is coarse).  Measured
+// on the eight 13B and 175B layer shapes, it picks the faster of the two
+// four-wave forms on every one.
 static int best_tiled(int m, int n, double& best) {
-  int v = 6;
-  best = cost_tiled(6, m, n) * 0.97;
-  for (int c : {8, 7}) {
+  int v = 12;
+  best = cost_tiled(12, m, n) * 0.97;
+  for (int c : {13, 7}) {
     const double e = cost_tiled(c, m, n);
     if (e < best) {
       best = e;
@@ -728,7 +892,9 @@ static double cost_big_split(int m, int n, int k, SplitPlan& p) {
   p.tiles = (int)(ceil_div_l(m, 256) * ceil_div_l(n, 256));
   if (kt % 2) return best;
   for (int sp = 2; sp <= 4 && kt / sp >= 40; ++sp) {
-    const double c = ceil_div_l((long)p.tiles * sp, NUM_CU) * 65536.0 / sp * 1.15;
+    // the split GEMM runs on the eight-wave 256 x 256 tile (~0.9 of the
+    // four-wave rate), and its partial sums cost ~15% more
+    const double c = ceil_div_l((long)p.tiles * sp, NUM_CU) * 65536.0 / sp * 1.15 / 0.9;
     if (c < best) {
       best = c;
       set_splits(kt, sp, p);
@@ -743,7 +909,7 @@ static int plan_gemm(int m, int n, int k, SplitPlan& split) {
   int pinned = -1;
   if (const char* f = getenv("ORCA_GEMM_VARIANT")) {
     const int v = atoi(f);
-    if (v == 0 || v == 3 || v == 6 || v == 7 || v == 8 || v == 10 || v == 11) pinned = v;
+    if (v == 0 || v == 3 || v == 6 || v == 7 || v == 8 || (v >= 10 && v <= 13)) pinned = v;
   }
   if (pinned >= 0 && pinned != 10) return pinned;
   if (m >= 1 && k % BK == 0 && n % 4 == 0) {
@@ -757,9 +923,6 @@ static int plan_gemm(int m, int n, int k, SplitPlan& split) {
         return 10;
       }
     }
-    // long K: the wave-specialised 256 x 256 form (1.5-6% faster on the
-    // 175B layer shapes, K = 12288 and 49152; no gain at K = 5120)
-    if (v == 6 && k >= WS_MIN_K) return 11;
     return v;
   }
   return 7;
@@ -831,6 +994,24 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
           break;
         }
         [[fallthrough]];   // odd K steps or offsets past 2^31: the 256 x 256 form
+      case 12:
+      case 13:
+        if ((v == 12 || v == 13) && k >= 2 * BK && (k / BK) % 2 == 0 &&
+            (long)std::max(m, n) * k < (1L << 31)) {
+          const int bn = v == 12 ? 256 : 192;
+          const int tiles_m = (m + 255) / 256, tiles_n = (n + bn - 1) / bn;
+          auto kern = v == 12 ? gemm_w4_kernel<EPI, 4> : gemm_w4_kernel<EPI, 3>;
+          hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(W4_THREADS), 0, s,
+                             (const bf16*)a, (const bf16*)w, (const bf16*)bias, ep, m, n, k,
+                             tiles_m);
+          break;
+        }
+        if (v == 13) {   // odd K steps or offsets past 2^31: the 256 x 192 form
+          if ((k / BK) % 2 == 0) launch_mfma<EPI, 4, 2, 2, 3, true>(a, w, bias, ep, m, n, k, s);
+          else launch_mfma<EPI, 4, 2, 2, 3>(a, w, bias, ep, m, n, k, s);
+          break;
+        }
+        [[fallthrough]];
       case 6:
         if ((k / BK) % 2 == 0) launch_mfma<EPI, 4, 2, 2, 4, true>(a, w, bias, ep, m, n, k, s);
         else launch_mfma<EPI, 4, 2, 2, 4>(a, w, bias, ep, m, n, k, s);

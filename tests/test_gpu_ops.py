@@ -115,7 +115,7 @@ def test_linear(dtype, m, n, k, epi, workspace):
     assert rel_err(got, ref) < TOL[dtype]
 
 
-@pytest.mark.parametrize("variant", ["0", "3", "6", "7", "8", "10", "11"])
+@pytest.mark.parametrize("variant", ["0", "3", "6", "7", "8", "10", "11", "12", "13"])
 @pytest.mark.parametrize("m,n,k,epi", [
     (300, 1024, 1024, L.ORCA_EPI_BIAS_GELU), (520, 768, 2048, L.ORCA_EPI_BIAS_RESID),
     (64, 1536, 512, L.ORCA_EPI_BIAS), (33, 640, 2048, L.ORCA_EPI_BIAS_GELU)])
@@ -142,7 +142,8 @@ def test_linear_empty_batch_is_noop():
     ("bf16", 7, 256, 2, None), ("bf16", 133, 512, 8, None), ("bf16", 64, 1024, 8, None),
     ("f32", 7, 64, 4, None), ("f32", 70, 256, 8, None),
     ("bf16", 300, 512, 4, "6"), ("bf16", 300, 512, 4, "0"), ("bf16", 300, 512, 4, "10"),
-    ("bf16", 300, 512, 4, "8"), ("bf16", 300, 512, 4, "11"),
+    ("bf16", 300, 512, 4, "8"), ("bf16", 300, 512, 4, "11"), ("bf16", 300, 512, 4, "12"),
+    ("bf16", 300, 512, 4, "13"),
     ("bf16", 40, 1024, 8, "10")])
 def test_qkv_split_and_append(dtype, m, hidden, heads, variant, monkeypatch):
     if variant is not None:
