@@ -218,6 +218,115 @@ __device__ __forceinline__ void store_wave_tile(const f32x16_t (&acc)[TI][TJ],
   }
 }
 
+// The epilogue of a wave's (32*TI) x (32*TJ) accumulators computed
+// transposed (W as the MFMA's first operand, so each accumulator holds
+// C^T): for accumulator [i][j], lane l holds output row m0 + 32 i + l % 32,
+// and its registers 4 q .. 4 q + 3 hold the four consecutive columns
+// n0 + 32 j + 8 q + 4 (l / 32) + 0..3 of that row.  Each register group is
+// one 8-byte (bf16) or 16-byte (fp32) access, a quarter of the element-wise
+// stores, and the QKV pool slot is read once per row.  N is a multiple of
+// 64, so a 32-column block is inside the matrix or outside it whole.
+template <int EPI, int TI, int TJ>
+__device__ __forceinline__ void store_wave_tile_t(const f32x16_t (&acc)[TI][TJ],
+                                                  const bf16* __restrict__ bias,
+                                                  const EpiParams& ep, int M, int N, int m0,
+                                                  int n0, int lane) {
+  const int mr = lane & 31, nh = (lane >> 5) * 4;
+  float bq[TJ][4][4];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = min(n0 + 32 * j + 8 * q + nh, N - 4);
+      const uint2 w = EPI == EPI_PARTIAL ? make_uint2(0u, 0u)
+                                         : *reinterpret_cast<const uint2*>(bias + n);
+      bq[j][q][0] = bf16_lo(w.x);
+      bq[j][q][1] = bf16_hi(w.x);
+      bq[j][q][2] = bf16_lo(w.y);
+      bq[j][q][3] = bf16_hi(w.y);
+    }
+  if constexpr (EPI == ORCA_EPI_BIAS_RESID) {
+    // fp32 read-modify-write.  The compiler cannot prove that the reads and
+    // writes do not alias, so it keeps them in program order: each row
+    // block's reads are issued before the previous block's writes, and one
+    // memory latency is exposed per tile rather than per row block.
+    float4 cur[TJ][4], nxt[TJ][4];
+#define ORCA_RESID_READ(DST, I)                                                               \
+  {                                                                                           \
+    const float* row = static_cast<const float*>(ep.out) +                                    \
+                       (size_t)min(m0 + 32 * (I) + mr, M - 1) * ep.ldo;                      \
+    _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                            \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) DST[j][q] =                             \
+            *reinterpret_cast<const float4*>(row + min(n0 + 32 * j + 8 * q + nh, N - 4));     \
+  }
+    ORCA_RESID_READ(cur, 0)
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      if (i + 1 < TI) ORCA_RESID_READ(nxt, i + 1)
+      __builtin_amdgcn_sched_barrier(0);
+      const int m = m0 + 32 * i + mr;
+      float* const row = static_cast<float*>(ep.out) + (size_t)min(m, M - 1) * ep.ldo;
+      if (m < M) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          if (n0 + 32 * j >= N) continue;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float4 v = cur[j][q];
+            v.x += acc[i][j][4 * q] + bq[j][q][0];
+            v.y += acc[i][j][4 * q + 1] + bq[j][q][1];
+            v.z += acc[i][j][4 * q + 2] + bq[j][q][2];
+            v.w += acc[i][j][4 * q + 3] + bq[j][q][3];
+            *reinterpret_cast<float4*>(row + n0 + 32 * j + 8 * q + nh) = v;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < TI) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) cur[j][q] = nxt[j][q];
+      }
+    }
+#undef ORCA_RESID_READ
+    return;
+  }
+  // the QKV pool slots of the lane's rows, read before any write
+  int slots[TI];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+    slots[i] = EPI == EPI_QKV ? ep.qkv.row_dst[min(m0 + 32 * i + mr, M - 1)] : 0;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int m = m0 + 32 * i + mr, slot = slots[i];
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      if (n0 + 32 * j >= N) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + 32 * j + 8 * q + nh;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[i][j][4 * q + e] + bq[j][q][e];
+          if constexpr (EPI == ORCA_EPI_BIAS_GELU) v[e] = gelu_tanh(v[e]);
+        }
+        if constexpr (EPI == EPI_PARTIAL) {
+          *reinterpret_cast<float4*>(static_cast<float*>(ep.out) + (size_t)m * ep.ldo + n) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          // the four columns lie in one head of one block (d % 4 == 0)
+          const EpiCol<bf16, EPI> col(ep, n);
+          *reinterpret_cast<uint2*>(col.ptr + (size_t)(col.slot ? slot : m) * col.stride) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+      }
+    }
+  }
+}
+
 // STREAM_W: W is read by one row tile only (the few-rows path), so its
 // loads carry the non-temporal hint; otherwise W panels are re-read by the
 // other row tiles through L2 and load plainly.
@@ -585,10 +694,11 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
       *reinterpret_cast<const bf16x8_t*>(&sA[BUF][a_off + i * 32 * LDK + (KS) * 16]);         \
   _Pragma("unroll") for (int j = 0; j < TJ; ++j) FB[j] =                                      \
       *reinterpret_cast<const bf16x8_t*>(&sB[BUF][b_off + j * 32 * LDK + (KS) * 16]);
+  // W as the first operand: each accumulator holds C^T (see store_wave_tile_t)
 #define ORCA_W4_MFMA(FA, FB)                                                                  \
   _Pragma("unroll") for (int i = 0; i < TI; ++i)                                              \
       _Pragma("unroll") for (int j = 0; j < TJ; ++j) acc[i][j] =                              \
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB[j], acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[j], FA[i], acc[i][j], 0, 0, 0);
   // step kt (LDS buffer CUR): loads of step kt+2 into LS, step kt+1 from SS
   // into the other buffer, then the four sub-steps with the barrier before
   // the last one's MFMAs
@@ -655,8 +765,8 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
 #undef ORCA_W4_FRAGS
 #undef ORCA_W4_LOAD
 #undef ORCA_W4_STORE
-  store_wave_tile<EPI, TI, TJ>(acc, bias, ep, M, N, tm * BM + wm * 32 * TI,
-                               tn * BN + wn * 32 * TJ, lane);
+  store_wave_tile_t<EPI, TI, TJ>(acc, bias, ep, M, N, tm * BM + wm * 32 * TI,
+                                 tn * BN + wn * 32 * TJ, lane);
 }
 
 // ---------------------------------------------------------------- few rows
