@@ -112,7 +112,7 @@ def measured_traffic(workload, key, files):
 
 
 # kernels each timed region launches, as rocprofv3 names them
-TRAFFIC_KERNELS = {"gemm": ("gemm_bf16", "gemm_ws", "gemm_f32", "skinny_reduce"),
+TRAFFIC_KERNELS = {"gemm": ("gemm_bf16", "gemm_w4", "gemm_ws", "gemm_f32", "skinny_reduce"),
                    "decode": ("attn_split", "attn_combine"), "copy": ("copyBuffer",)}
 
 
@@ -286,10 +286,10 @@ def main():
         if tr:
             kname = tr["kernel"]
         elif bf16:
-            # the launch planner's choice: split-K for few rows, the
-            # wave-specialised 256 x 256 kernel from K = 8192 on
+            # the launch planner's choice: split-K for few rows, otherwise
+            # the four-wave 256 x 256 or 256 x 192 tile
             kname = ("gemm_bf16_kernel<gelu> split-K + skinny_reduce_kernel<gelu>" if split
-                     else "gemm_ws_kernel<gelu>" if H >= 8192 else "gemm_bf16_kernel<gelu>")
+                     else "gemm_w4_kernel<gelu>")
         else:
             kname = "gemm_f32_kernel<gelu>"
         common = {"kernel": kname + " (FFN1)", "shape": [M, F, H],
