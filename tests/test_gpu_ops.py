@@ -129,6 +129,38 @@ def test_linear_every_variant(variant, m, n, k, epi, monkeypatch):
     assert rel_err(got, ref) < TOL["bf16"]
 
 
+# edges of the four-wave tiles (variants 12: 256 x 256, 13: 256 x 192): the
+# shortest K (two steps), an odd step count (falls back to the eight-wave
+# form), one row, rows and columns that end inside a tile
+@pytest.mark.parametrize("variant", ["12", "13"])
+@pytest.mark.parametrize("m,n,k", [(1, 128, 128), (257, 448, 128), (300, 640, 192),
+                                   (513, 1344, 384), (2176, 1024, 640)])
+@pytest.mark.parametrize("epi", [L.ORCA_EPI_BIAS, L.ORCA_EPI_BIAS_GELU, L.ORCA_EPI_BIAS_RESID])
+def test_four_wave_edges(variant, m, n, k, epi, monkeypatch):
+    print(f"case four-wave variant {variant} m={m} n={n} k={k} epi={epi}", flush=True)
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", variant)
+    got, ref, _ = _linear_case("bf16", m, n, k, epi, False)
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("variant", ["12", "13"])
+def test_four_wave_is_deterministic(variant, monkeypatch):
+    """Two launches on the same inputs give the same bits."""
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", variant)
+    m, n, k = 700, 1536, 1024
+    rng = np.random.default_rng(7)
+    a = dev(draw(rng, (m, k), 1.0, "bf16"), "bf16")
+    w = dev(draw(rng, (n, k), 0.02, "bf16"), "bf16")
+    b = dev(draw(rng, n, 0.02, "bf16"), "bf16")
+    outs = []
+    for _ in range(2):
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+        L.orca_op_linear(L.ORCA_BF16, L.ORCA_EPI_BIAS_GELU, a, w, b, out, m, n, k)
+        outs.append(out.view(torch.int16).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+
+
 def test_linear_empty_batch_is_noop():
     out = torch.full((4, 128), 3.0, device=DEV)
     a = torch.zeros((4, 64), device=DEV, dtype=torch.bfloat16)
@@ -143,7 +175,7 @@ def test_linear_empty_batch_is_noop():
     ("f32", 7, 64, 4, None), ("f32", 70, 256, 8, None),
     ("bf16", 300, 512, 4, "6"), ("bf16", 300, 512, 4, "0"), ("bf16", 300, 512, 4, "10"),
     ("bf16", 300, 512, 4, "8"), ("bf16", 300, 512, 4, "11"), ("bf16", 300, 512, 4, "12"),
-    ("bf16", 300, 512, 4, "13"),
+    ("bf16", 300, 512, 4, "13"), ("bf16", 257, 768, 6, "12"), ("bf16", 70, 1024, 16, "13"),
     ("bf16", 40, 1024, 8, "10")])
 def test_qkv_split_and_append(dtype, m, hidden, heads, variant, monkeypatch):
     if variant is not None:
