@@ -10,16 +10,19 @@
 // K, H of V); the split before attention and the K/V append are index
 // arithmetic.  0h-n0.github.io digest, implementation notes: fused GeLU.
 //
-// bf16 path: MFMA (v_mfma_f32_32x32x16_bf16) with fp32 accumulation.
-// Workgroup tiles of 256 x 256 (eight waves, each 64 x 128) or 128 x 128
-// (four waves, each 64 x 64), K step 64.  Both operands are K-contiguous in HBM (A is
-// [M][K], W is [N][K]), loaded with 16-byte coalesced loads into registers,
-// then into a double-buffered LDS stage padded by 16 bytes per row so the
-// 16-byte fragment reads of a wave hit distinct banks.  One barrier per K
-// step: the loads of step k+1 are in flight while step k runs on the MFMAs.
-// The workgroup index is remapped so that each of the 8 XCDs (one L2 each)
-// walks a contiguous range of tiles, M fastest, so the W column panel a tile
-// needs is shared by the tiles resident on the same XCD.
+// bf16 path: MFMA (v_mfma_f32_32x32x16_bf16) with fp32 accumulation, K step
+// 64.  Both operands are K-contiguous in HBM (A is [M][K], W is [N][K]),
+// loaded with 16-byte coalesced loads into registers, then into a
+// double-buffered LDS stage padded by 16 bytes per row so the 16-byte
+// fragment reads of a wave hit distinct banks; one barrier per K step.  The
+// large Linear layers run on the four-wave kernel (256 x 256 or 256 x 192
+// tiles, one wave per SIMD with its accumulators in the accumulation
+// registers, the K step's traffic spread over its MFMAs); the eight-wave
+// kernel (256 x 256 / 256 x 192 / 128 x 128 tiles) serves the few-rows
+// split-K path and the fallbacks.  The workgroup index is remapped so that
+// each of the 8 XCDs (one L2 each) walks a contiguous range of tiles, M
+// fastest, so the W column panel a tile needs is shared by the tiles
+// resident on the same XCD.
 //
 // fp32 path: a plain LDS-tiled FMA kernel (64 x 64 tile) for fp32 models.
 #include <math.h>
