@@ -78,6 +78,9 @@ def test_h1024_two_layer_bf16():
     # and a whole prompt: prefill tiles with the key range shifted by kv_len
     (2, 512, 4, 1024, "bf16", [1, 200, 1, 77, 50], [300, 130, 5, 1000, 0]),
     (1, 256, 2, 512, "bf16", [129, 1, 255], [1, 64, 513]),
+    # a whole 700-token prompt beside increments: six query tiles, the last
+    # ones walking 10-11 key steps
+    (1, 256, 2, 512, "bf16", [700, 1, 1], [0, 50, 900]),
     (2, 256, 2, 512, "f32", [1, 40, 3, 17], [50, 70, 600, 0]),
 ])
 def test_custom_mixed_batches(layers, hidden, heads, ffn, dtype, q, kv):
