@@ -657,7 +657,10 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
   typedef uint32_t U4 __attribute__((ext_vector_type(4)));
   Stage s0, s1;
   // buffer loads: a 32-bit lane offset plus the K step's offset in a scalar
-  // register, so no 64-bit address is formed per load
+  // register, so no 64-bit address is formed per load.  The resource's last
+  // word (0x00020000) selects raw 32-bit data, as gfx9-family raw buffer
+  // loads expect; num_records is the operand's size (the clamped offsets
+  // never reach past it, and a read past it would return zeros)
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
       (void*)A, (short)0, (int)(uint32_t)std::min<size_t>((size_t)M * K * 2, 0xffffffffu),
       0x00020000);
