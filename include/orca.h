@@ -223,6 +223,15 @@ typedef enum {
  * differs.  orca_op_linear_workspace_bytes returns 0 where split-K does not
  * apply (fp32, or enough tiles). */
 size_t orca_op_linear_workspace_bytes(int32_t dtype, int32_t m, int32_t n, int32_t k);
+/* The kernel form orca_op_linear takes for this problem, without launching
+ * anything (host only): the launch planner's choice after the fallbacks,
+ * the ORCA_GEMM_VARIANT environment override included.  bf16: 12 and 13 the
+ * four-wave 256x256 and 256x192 tiles, 7 the eight-wave 128x128 tile, 6 and
+ * 8 the eight-wave 256x256 and 256x192 tiles, 10 split-K (when the call
+ * brings orca_op_linear_workspace_bytes of workspace), 0, 3 and 11 pinned
+ * forms; -1 for fp32 (the FMA kernel); -2 for shapes orca_op_linear
+ * rejects. */
+int32_t orca_op_linear_variant(int32_t dtype, int32_t m, int32_t n, int32_t k);
 orca_status orca_op_linear(int32_t dtype, int32_t epilogue, const void* a, const void* w,
                            const void* bias, void* out, int32_t m, int32_t n, int32_t k,
                            void* workspace, size_t ws_bytes, void* stream);

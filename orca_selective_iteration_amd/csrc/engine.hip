@@ -436,6 +436,12 @@ orca_status orca_op_layernorm(int32_t dtype, const float* x, const void* gamma, 
   return ORCA_OK;
 }
 
+int32_t orca_op_linear_variant(int32_t dtype, int32_t m, int32_t n, int32_t k) {
+  if ((dtype != ORCA_BF16 && dtype != ORCA_F32) || m < 1 || n < 64 || k < 64 || n % 64 || k % 64)
+    return -2;
+  return linear_plan_variant(dtype, m, n, k);
+}
+
 size_t orca_op_linear_workspace_bytes(int32_t dtype, int32_t m, int32_t n, int32_t k) {
   if (m < 0 || n < 64 || k < 64 || n % 64 || k % 64) return 0;
   return linear_workspace_bytes(dtype, m, n, k);

@@ -1044,6 +1044,19 @@ static int plan_gemm(int m, int n, int k, SplitPlan& split) {
   return 7;
 }
 
+int linear_plan_variant(int dtype, int m, int n, int k) {
+  if (dtype != ORCA_BF16) return -1;   // the fp32 FMA kernel
+  SplitPlan sp{};
+  const int v = plan_gemm(m, n, k, sp);
+  const bool even = (k / BK) % 2 == 0;
+  switch (v) {
+    case 11: return even && (long)std::max(m, n) * k < (1L << 31) ? 11 : (even ? 6 : 3);
+    case 12: return even && k >= 2 * BK && (long)std::max(m, n) * k < (1L << 31) ? 12 : (even ? 6 : 3);
+    case 13: return even && k >= 2 * BK && (long)std::max(m, n) * k < (1L << 31) ? 13 : 8;
+    default: return v;
+  }
+}
+
 size_t linear_workspace_bytes(int dtype, int m, int n, int k) {
   SplitPlan p;
   if (dtype != ORCA_BF16 || m < 1 || plan_gemm(m, n, k, p) != 10) return 0;

@@ -41,6 +41,10 @@ constexpr int EPI_PARTIAL = 4;
 constexpr int SPLIT_MAX_M = 1024;
 constexpr int SPLIT_MAX_SPLITS = 16;
 size_t linear_workspace_bytes(int dtype, int m, int n, int k);
+// The tile variant a bf16 launch of this problem takes (ORCA_GEMM_VARIANT
+// honoured, fallbacks applied; 10 is split-K given its workspace); -1 for
+// fp32.
+int linear_plan_variant(int dtype, int m, int n, int k);
 hipError_t launch_linear(int dtype, int epilogue, const void* a, const void* w, const void* bias,
                          void* out, const QkvDest* qkv, int m, int n, int k, void* ws,
                          size_t ws_bytes, hipStream_t s);

@@ -242,6 +242,36 @@ def test_op_validation_fails_before_gpu():
     assert e.value.status == L.ORCA_ERR_UNSUPPORTED          # head dim 32 in bf16
 
 
+# the launch planner's kernel form (orca_op_linear_variant, host only): the
+# forms measured fastest on MI355X at these shapes (12 / 13: four-wave
+# 256 x 256 / 256 x 192; 10: split-K; 7: eight-wave 128 x 128), and the
+# fallbacks of an odd K-step count (13 -> 8, 12 -> 6 -> 3)
+@pytest.mark.parametrize("m,n,k,variant", [
+    (2176, 15360, 5120, 13), (2176, 5120, 5120, 13),        # 13B QKV, output projection
+    (2176, 20480, 5120, 12), (2176, 5120, 20480, 13),       # 13B FFN1, FFN2
+    (3698, 36864, 12288, 12), (3698, 12288, 12288, 12),     # 175B layer shapes
+    (3698, 49152, 12288, 12), (3698, 12288, 49152, 12),
+    (64, 15360, 5120, 10), (64, 20480, 5120, 10),           # few rows: split-K
+    (1100, 15360, 5120, 13), (1100, 20480, 5120, 12), (1100, 5120, 5120, 10),
+    (1600, 15360, 5120, 12), (1600, 20480, 5120, 13), (1600, 5120, 20480, 13),
+    (2176, 15360, 5184, 8), (2176, 20480, 5184, 3),         # 81 K steps
+])
+def test_planner_variant(m, n, k, variant, monkeypatch):
+    monkeypatch.delenv("ORCA_GEMM_VARIANT", raising=False)
+    assert L.orca_op_linear_variant(L.ORCA_BF16, m, n, k) == variant
+
+
+def test_planner_variant_pin_and_rejects(monkeypatch):
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", "7")
+    assert L.orca_op_linear_variant(L.ORCA_BF16, 2176, 20480, 5120) == 7
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", "12")
+    assert L.orca_op_linear_variant(L.ORCA_BF16, 300, 1024, 192) == 3   # 3 K steps: 6, then 3
+    monkeypatch.delenv("ORCA_GEMM_VARIANT")
+    assert L.orca_op_linear_variant(L.ORCA_F32, 64, 128, 64) == -1
+    assert L.orca_op_linear_variant(L.ORCA_BF16, 64, 100, 64) == -2
+    assert L.orca_op_linear_variant(L.ORCA_BF16, 0, 128, 64) == -2
+
+
 # the launch planner's split-K choice, seen through the workspace it asks for
 # (split-K planes are fp32 [splits][m][n]; 0 bytes means a tiled launch)
 @pytest.mark.parametrize("m,n,k,splits", [
