@@ -110,6 +110,26 @@ __device__ __forceinline__ int xcd_remap(int b, int nblk) {
   return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
+// Tile (tm, tn) of a launch-order index.  group <= 0: row tiles fastest
+// (an XCD's concurrent workgroups cover every row tile of one or two column
+// panels).  Otherwise the row tiles are taken in groups of `group`, and
+// inside a group row tiles fastest, then column panels: an XCD's concurrent
+// workgroups then share `group` A row panels and about 32 / group W column
+// panels through its L2.
+__device__ __forceinline__ void tile_of(int logical, int tiles_m, int ntiles, int group, int& tm,
+                                        int& tn) {
+  if (group <= 0 || group >= tiles_m) {
+    tm = logical % tiles_m;
+    tn = logical / tiles_m;
+    return;
+  }
+  const int per_group = group * (ntiles / tiles_m);
+  const int g = logical / per_group, idx = logical - g * per_group;
+  const int gm = min(group, tiles_m - g * group);
+  tm = g * group + idx % gm;
+  tn = idx / gm;
+}
+
 // Workgroup tile (WGM*32*TI) x (WGN*32*TJ): a WGM x WGN grid of waves, each
 // owning (32*TI) x (32*TJ) outputs as TI x TJ 32x32 MFMA accumulators.
 template <int WGM, int WGN, int TI, int TJ>
@@ -628,7 +648,7 @@ template <int EPI, int TJ>
 __global__ __launch_bounds__(W4_THREADS, 1)
 void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
                     const bf16* __restrict__ bias, EpiParams ep, int M, int N, int K,
-                    int tiles_m) {
+                    int tiles_m, int group_m) {
   constexpr int TI = 4, BM = 256, BN = 64 * TJ;
   // 16-byte chunks per lane and K step: LA of A rows, then LB of W rows
   constexpr int LA = BM * 8 / W4_THREADS, LB = BN * 8 / W4_THREADS, NC = LA + LB;
@@ -636,7 +656,8 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDK];
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int tm = logical % tiles_m, tn = logical / tiles_m;
+  int tm, tn;
+  tile_of(logical, tiles_m, gridDim.x, group_m, tm, tn);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -771,6 +792,185 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
 #undef ORCA_W4_FRAGS
 #undef ORCA_W4_LOAD
 #undef ORCA_W4_STORE
+  store_wave_tile_t<EPI, TI, TJ>(acc, bias, ep, M, N, tm * BM + wm * 32 * TI,
+                                 tn * BN + wn * 32 * TJ, lane);
+}
+
+// --------------------------------- one wave per SIMD, operands DMA'd to LDS
+
+// The same 256 x (64 TJ) tile on four waves, with the operands moved from
+// HBM straight into LDS by the buffer loads' LDS mode (gfx950 moves 16
+// bytes per lane this way): no staging registers, no LDS write
+// instructions.  K step 32, four LDS stages, so the loads of step kt+4 are
+// issued three steps before they are read.  A load writes lane l's 16 bytes
+// at (M0 + 16 l), so the LDS layout follows the lane order: 64-byte rows
+// (32 bf16 of one K step) with the four 16-byte chunks of row r permuted by
+// XOR with swz(r) = ((r >> 1) ^ (r >> 3)) & 3, which spreads the eight (or
+// sixteen) rows one ds_read_b128 serves over distinct LDS banks; each lane
+// loads the global chunk that belongs at its LDS slot.
+typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, size_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  rsrc_t r;
+  r.x = (uint32_t)p;
+  r.y = (uint32_t)(p >> 32) & 0xffffu;   // stride 0
+  r.z = (uint32_t)std::min<size_t>(bytes, 0xffffffffu);
+  r.w = 0x00020000u;                     // raw 32-bit data (gfx9 family)
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One 16-byte-per-lane buffer load into LDS at lds + 16 * lane.  Written as
+// assembly so that the compiler does not count it among the LDS writes it
+// orders: with the builtin it waits for every load in flight before each LDS
+// read, which serialises the stages.  The caller waits (vmcnt) and meets the
+// workgroup barrier before reading what it wrote.  M0 is restored.
+__device__ __forceinline__ void dma_b128(const rsrc_t& r, uint32_t lds, uint32_t voff,
+                                         uint32_t soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+      : "memory");
+}
+
+// s_waitcnt for the vector-memory counter only
+#define ORCA_WAIT_VMCNT(N) \
+  __builtin_amdgcn_s_waitcnt(((N) & 0xf) | (((N) >> 4) << 14) | (0x7 << 4) | (0xf << 8))
+
+template <int EPI, int TJ, int DK>
+__global__ __launch_bounds__(W4_THREADS, 1)
+void gemm_d4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
+                    const bf16* __restrict__ bias, EpiParams ep, int M, int N, int K,
+                    int tiles_m, int group_m) {
+  constexpr int TI = 4, BM = 256, BN = 64 * TJ;
+  constexpr int ROWB = DK * 2;                    // bytes per row and K step
+  constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
+  constexpr int RPI = 1024 / ROWB;                // rows one 1 KB load fills
+  constexpr int NS = DK == 32 ? 4 : 2;            // LDS stages
+  constexpr int NSUB = DK / 16;                   // MFMA sub-steps per K step
+  constexpr int STAGE = (BM + BN) * ROWB;         // bytes per stage
+  constexpr int NIW = (BM + BN) / (4 * RPI);      // 1 KB loads per wave and stage
+  constexpr int NM = TI * TJ, NR = TI + TJ;
+  static_assert(DK == 32 || DK == 64, "K step");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  int tm, tn;
+  tile_of(logical, tiles_m, gridDim.x, group_m, tm, tn);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int KT = K / DK;
+  // chunk permutation of LDS row r (a function of r mod 32): the rows one
+  // ds_read_b128 serves land in distinct banks for 8 and for 16 lanes
+  auto swz = [](int r) {
+    return DK == 32 ? ((r >> 1) ^ (r >> 3)) & 3 : (r ^ ((r >> 3) & 3)) & 7;
+  };
+
+  const rsrc_t rA = buffer_rsrc(A, (size_t)M * K * 2);
+  const rsrc_t rB = buffer_rsrc(W, (size_t)N * K * 2);
+  // load j of this wave fills stage rows RPI c .. RPI c + RPI-1, c = 4 j +
+  // wave (rows 0 .. BM-1 hold A, the rest W); lane l takes row RPI c +
+  // l / CPR and LDS chunk l % CPR, which holds the row's global chunk
+  // (l % CPR) ^ swz(row)
+  uint32_t voff[NIW];
+#pragma unroll
+  for (int j = 0; j < NIW; ++j) {
+    const int r = RPI * (4 * j + wave) + lane / CPR;
+    const int c = (lane % CPR) ^ swz(r);
+    const int g = j < BM / (4 * RPI) ? min(tm * BM + r, M - 1) : min(tn * BN + r - BM, N - 1);
+    voff[j] = (uint32_t)g * (uint32_t)K * 2u + (uint32_t)c * 16u;
+  }
+  const uint32_t lds0 = lds_address(smem) + (uint32_t)wave * 1024u;
+#define ORCA_D4_LOAD(J, ST, KS)                                                               \
+  dma_b128((J) < BM / (4 * RPI) ? rA : rB, lds0 + (ST) * STAGE + (J) * 4096, voff[J],         \
+           (KS) * ROWB)
+
+  // fragment reads: lane row fr, sub-step ks takes logical chunk 2 ks + h
+  const int fr = lane & 31, h = lane >> 5, sw = swz(fr);
+  int ro[NSUB];
+#pragma unroll
+  for (int ks = 0; ks < NSUB; ++ks) ro[ks] = fr * ROWB + ((2 * ks + h) ^ sw) * 16;
+  const uint8_t* fa_base = smem + (wm * 32 * TI) * ROWB;
+  const uint8_t* fb_base = smem + (BM + wn * 32 * TJ) * ROWB;
+#define ORCA_D4_FRAG(U, FA, FB, ST, RO)                                                       \
+  if ((U) < TI)                                                                              \
+    FA[(U) < TI ? (U) : 0] = *reinterpret_cast<const bf16x8_t*>(                              \
+        fa_base + (ST) * STAGE + (U) * 32 * ROWB + (RO));                                     \
+  else if ((U) < NR)                                                                         \
+    FB[(U) < NR && (U) >= TI ? (U) - TI : 0] = *reinterpret_cast<const bf16x8_t*>(            \
+        fb_base + (ST) * STAGE + ((U) - TI) * 32 * ROWB + (RO));
+#define ORCA_D4_MFMA(U, FA, FB)                                                               \
+  acc[(U) / TJ][(U) % TJ] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                          \
+      FB[(U) % TJ], FA[(U) / TJ], acc[(U) / TJ][(U) % TJ], 0, 0, 0);
+
+  f32x16_t acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  bf16x8_t fa0[TI], fb0[TJ], fa1[TI], fb1[TJ];
+
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) ORCA_D4_LOAD(j, st, min(st, KT - 1));
+  ORCA_WAIT_VMCNT((NS - 1) * NIW);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < NR; ++u) { ORCA_D4_FRAG(u, fa0, fb0, 0, ro[0]) }
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt % NS, nst = (kt + 1) % NS;
+    // sub-steps 0 .. NSUB-2: each one's MFMAs with the next one's fragment
+    // reads (two register sets, alternating)
+#pragma unroll
+    for (int ks = 0; ks + 1 < NSUB; ++ks) {
+#pragma unroll
+      for (int u = 0; u < NM; ++u) {
+        if (ks % 2 == 0) {
+          ORCA_D4_FRAG(u, fa1, fb1, st, ro[ks + 1])
+          ORCA_D4_MFMA(u, fa0, fb0)
+        } else {
+          ORCA_D4_FRAG(u, fa0, fb0, st, ro[ks + 1])
+          ORCA_D4_MFMA(u, fa1, fb1)
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // this wave's loads of step kt+1 have landed (later steps may still be
+    // in flight); after the barrier every wave's have, and no wave reads
+    // stage st any more
+    ORCA_WAIT_VMCNT((NS - 2) * NIW);
+    __syncthreads();
+    // the last sub-step's MFMAs, with the loads of step kt+NS into stage st
+    // and the reads of the next step's first fragments
+#pragma unroll
+    for (int u = 0; u < NM; ++u) {
+#pragma unroll
+      for (int j = u * NIW / NM; j < (u + 1) * NIW / NM; ++j)
+        ORCA_D4_LOAD(j, st, min(kt + NS, KT - 1));
+      ORCA_D4_FRAG(u, fa0, fb0, nst, ro[0])
+      ORCA_D4_MFMA(u, fa1, fb1)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  ORCA_WAIT_VMCNT(0);
+#undef ORCA_D4_MFMA
+#undef ORCA_D4_FRAG
+#undef ORCA_D4_LOAD
   store_wave_tile_t<EPI, TI, TJ>(acc, bias, ep, M, N, tm * BM + wm * 32 * TI,
                                  tn * BN + wn * 32 * TJ, lane);
 }
@@ -1006,6 +1206,9 @@ static double cost_big_split(int m, int n, int k, SplitPlan& p) {
   double best = 1e300;
   p.tile = 3;
   p.tiles = (int)(ceil_div_l(m, 256) * ceil_div_l(n, 256));
+  // no split unless a candidate below fills the plan
+  p.splits = 1;
+  p.kt_per_split = kt;
   if (kt % 2) return best;
   for (int sp = 2; sp <= 4 && kt / sp >= 40; ++sp) {
     // the split GEMM runs on the eight-wave 256 x 256 tile (~0.9 of the
@@ -1019,20 +1222,28 @@ static double cost_big_split(int m, int n, int k, SplitPlan& p) {
   return best;
 }
 
+// Row-tile group of the four-wave launches (tile_of): groups of 8 when the
+// launch has at least 12 row tiles (MI355X, 175B layer shapes at 3,698
+// rows: 1-3% faster than row tiles fastest; at 13B's 9 row tiles it made no
+// difference).  ORCA_GEMM_GROUP overrides it for sweeps.
+static int raster_group(int tiles_m) {
+  return env_int("ORCA_GEMM_GROUP", tiles_m >= 12 ? 8 : 0);
+}
+
 // The launch for one bf16 problem: a tiled variant, or split-K (`split`
 // filled, variant 10).  ORCA_GEMM_VARIANT=<n> pins the variant.
 static int plan_gemm(int m, int n, int k, SplitPlan& split) {
   int pinned = -1;
   if (const char* f = getenv("ORCA_GEMM_VARIANT")) {
     const int v = atoi(f);
-    if (v == 0 || v == 3 || v == 6 || v == 7 || v == 8 || (v >= 10 && v <= 13)) pinned = v;
+    if (v == 0 || v == 3 || v == 6 || v == 7 || v == 8 || (v >= 10 && v <= 15)) pinned = v;
   }
   if (pinned >= 0 && pinned != 10) return pinned;
   if (m >= 1 && k % BK == 0 && n % 4 == 0) {
     if (few_rows_plan(m, n, k, split)) return 10;
     double best;
     const int v = best_tiled(m, n, best);
-    SplitPlan bs;
+    SplitPlan bs{};
     if (cost_big_split(m, n, k, bs) < best || pinned == 10) {
       if (bs.splits > 1 && bs.splits <= SPLIT_MAX_SPLITS) {
         split = bs;
@@ -1053,12 +1264,14 @@ int linear_plan_variant(int dtype, int m, int n, int k) {
     case 11: return even && (long)std::max(m, n) * k < (1L << 31) ? 11 : (even ? 6 : 3);
     case 12: return even && k >= 2 * BK && (long)std::max(m, n) * k < (1L << 31) ? 12 : (even ? 6 : 3);
     case 13: return even && k >= 2 * BK && (long)std::max(m, n) * k < (1L << 31) ? 13 : 8;
+    case 14: return (long)std::max(m, n) * k < (1L << 31) ? 14 : (even ? 6 : 3);
+    case 15: return (long)std::max(m, n) * k < (1L << 31) ? 15 : 8;
     default: return v;
   }
 }
 
 size_t linear_workspace_bytes(int dtype, int m, int n, int k) {
-  SplitPlan p;
+  SplitPlan p{};
   if (dtype != ORCA_BF16 || m < 1 || plan_gemm(m, n, k, p) != 10) return 0;
   return (size_t)p.splits * m * n * sizeof(float);
 }
@@ -1123,6 +1336,21 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
           break;
         }
         [[fallthrough]];   // odd K steps or offsets past 2^31: the 256 x 256 form
+      case 14:
+      case 15:
+        if ((long)std::max(m, n) * k < (1L << 31)) {
+          const int bn = v == 14 ? 256 : 192;
+          const int tiles_m = (m + 255) / 256, tiles_n = (n + bn - 1) / bn;
+          const bool k64 = env_int("ORCA_D4_K64", 0) != 0;
+          auto kern = v == 14 ? (k64 ? gemm_d4_kernel<EPI, 4, 64> : gemm_d4_kernel<EPI, 4, 32>)
+                              : (k64 ? gemm_d4_kernel<EPI, 3, 64> : gemm_d4_kernel<EPI, 3, 32>);
+          hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(W4_THREADS), 0, s,
+                             (const bf16*)a, (const bf16*)w, (const bf16*)bias, ep, m, n, k,
+                             tiles_m, raster_group(tiles_m));
+          break;
+        }
+        v = v == 14 ? 12 : 13;   // offsets past 2^31: the register-staged forms' fallbacks
+        [[fallthrough]];
       case 12:
       case 13:
         if ((v == 12 || v == 13) && k >= 2 * BK && (k / BK) % 2 == 0 &&
@@ -1132,7 +1360,7 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
           auto kern = v == 12 ? gemm_w4_kernel<EPI, 4> : gemm_w4_kernel<EPI, 3>;
           hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(W4_THREADS), 0, s,
                              (const bf16*)a, (const bf16*)w, (const bf16*)bias, ep, m, n, k,
-                             tiles_m);
+                             tiles_m, raster_group(tiles_m));
           break;
         }
         if (v == 13) {   // odd K steps or offsets past 2^31: the 256 x 192 form

@@ -266,6 +266,21 @@ def test_planner_variant_pin_and_rejects(monkeypatch):
     assert L.orca_op_linear_variant(L.ORCA_BF16, 2176, 20480, 5120) == 7
     monkeypatch.setenv("ORCA_GEMM_VARIANT", "12")
     assert L.orca_op_linear_variant(L.ORCA_BF16, 300, 1024, 192) == 3   # 3 K steps: 6, then 3
+    # the LDS-DMA forms take any K step count; past 2^31 elements they fall
+    # back like the register-staged ones
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", "14")
+    assert L.orca_op_linear_variant(L.ORCA_BF16, 300, 1024, 192) == 14
+    assert L.orca_op_linear_variant(L.ORCA_BF16, 300, 1 << 19, 4096) == 6
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", "15")
+    assert L.orca_op_linear_variant(L.ORCA_BF16, 300, 1024, 192) == 15
+    assert L.orca_op_linear_variant(L.ORCA_BF16, 300, 1 << 19, 4096) == 8
+    # split-K pinned where no split applies (an odd K-step count, too short a
+    # K for the 256 x 256 split): a tiled form and no workspace
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", "10")
+    assert L.orca_op_linear_variant(L.ORCA_BF16, 300, 1024, 192) in (7, 12, 13)
+    assert L.orca_op_linear_workspace_bytes(L.ORCA_BF16, 300, 1024, 192) == 0
+    assert L.orca_op_linear_variant(L.ORCA_BF16, 2176, 20480, 5184) in (3, 7, 8, 12, 13)
+    assert L.orca_op_linear_workspace_bytes(L.ORCA_BF16, 2176, 20480, 5184) == 0
     monkeypatch.delenv("ORCA_GEMM_VARIANT")
     assert L.orca_op_linear_variant(L.ORCA_F32, 64, 128, 64) == -1
     assert L.orca_op_linear_variant(L.ORCA_BF16, 64, 100, 64) == -2

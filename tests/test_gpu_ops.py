@@ -115,7 +115,8 @@ def test_linear(dtype, m, n, k, epi, workspace):
     assert rel_err(got, ref) < TOL[dtype]
 
 
-@pytest.mark.parametrize("variant", ["0", "3", "6", "7", "8", "10", "11", "12", "13"])
+@pytest.mark.parametrize("variant", ["0", "3", "6", "7", "8", "10", "11", "12", "13", "14",
+                                     "15"])
 @pytest.mark.parametrize("m,n,k,epi", [
     (300, 1024, 1024, L.ORCA_EPI_BIAS_GELU), (520, 768, 2048, L.ORCA_EPI_BIAS_RESID),
     (64, 1536, 512, L.ORCA_EPI_BIAS), (33, 640, 2048, L.ORCA_EPI_BIAS_GELU)])
@@ -129,12 +130,14 @@ def test_linear_every_variant(variant, m, n, k, epi, monkeypatch):
     assert rel_err(got, ref) < TOL["bf16"]
 
 
-# edges of the four-wave tiles (variants 12: 256 x 256, 13: 256 x 192): the
-# shortest K (two steps), an odd step count (falls back to the eight-wave
-# form), one row, rows and columns that end inside a tile
-@pytest.mark.parametrize("variant", ["12", "13"])
-@pytest.mark.parametrize("m,n,k", [(1, 128, 128), (257, 448, 128), (300, 640, 192),
-                                   (513, 1344, 384), (2176, 1024, 640)])
+# edges of the four-wave tiles (variants 12 and 14: 256 x 256, 13 and 15:
+# 256 x 192; 14 and 15 load through LDS DMA in 32-wide K steps): the
+# shortest K (one 64-wide step: fewer K steps than LDS stages), an odd step
+# count (12 and 13 fall back to the eight-wave form), one row, rows and
+# columns that end inside a tile
+@pytest.mark.parametrize("variant", ["12", "13", "14", "15"])
+@pytest.mark.parametrize("m,n,k", [(1, 128, 128), (100, 256, 64), (257, 448, 128),
+                                   (300, 640, 192), (513, 1344, 384), (2176, 1024, 640)])
 @pytest.mark.parametrize("epi", [L.ORCA_EPI_BIAS, L.ORCA_EPI_BIAS_GELU, L.ORCA_EPI_BIAS_RESID])
 def test_four_wave_edges(variant, m, n, k, epi, monkeypatch):
     print(f"case four-wave variant {variant} m={m} n={n} k={k} epi={epi}", flush=True)
@@ -144,7 +147,7 @@ def test_four_wave_edges(variant, m, n, k, epi, monkeypatch):
     assert rel_err(got, ref) < TOL["bf16"]
 
 
-@pytest.mark.parametrize("variant", ["12", "13"])
+@pytest.mark.parametrize("variant", ["12", "13", "14", "15"])
 def test_four_wave_is_deterministic(variant, monkeypatch):
     """Two launches on the same inputs give the same bits."""
     monkeypatch.setenv("ORCA_GEMM_VARIANT", variant)
@@ -176,7 +179,8 @@ def test_linear_empty_batch_is_noop():
     ("bf16", 300, 512, 4, "6"), ("bf16", 300, 512, 4, "0"), ("bf16", 300, 512, 4, "10"),
     ("bf16", 300, 512, 4, "8"), ("bf16", 300, 512, 4, "11"), ("bf16", 300, 512, 4, "12"),
     ("bf16", 300, 512, 4, "13"), ("bf16", 257, 768, 6, "12"), ("bf16", 70, 1024, 16, "13"),
-    ("bf16", 40, 1024, 8, "10")])
+    ("bf16", 40, 1024, 8, "10"), ("bf16", 300, 512, 4, "14"), ("bf16", 300, 512, 4, "15"),
+    ("bf16", 257, 768, 6, "14"), ("bf16", 70, 1024, 16, "15")])
 def test_qkv_split_and_append(dtype, m, hidden, heads, variant, monkeypatch):
     if variant is not None:
         monkeypatch.setenv("ORCA_GEMM_VARIANT", variant)
