@@ -131,7 +131,11 @@ typedef struct {
  *   q_offset, q_len  rows [q_offset, q_offset+q_len) of the flattened
  *                    [sum L, H] input; offsets must be contiguous from 0
  *   kv_len           K/V entries cached before this iteration
- *   phase            ORCA_INITIATION (kv_len == 0) or ORCA_INCREMENT
+ *   phase            ORCA_INITIATION: prompt rows; kv_len == 0 for a whole
+ *                    prompt, or the tokens earlier chunks of the same prompt
+ *                    cached when a prompt is split over iterations (chunked
+ *                    prefill: [ultralytics] limits and combined techniques);
+ *                    ORCA_INCREMENT: one new token over its cache
  *                    (kv_len >= 1, q_len == 1)
  *   kv_base          first pool slot of the request's reservation; its
  *                    entry t lives in slot kv_base + t; this iteration
@@ -188,6 +192,34 @@ size_t orca_workspace_bytes(const orca_ctx* ctx);
 orca_status orca_iteration(orca_ctx* ctx, const orca_req_desc* reqs, int32_t n_reqs,
                            const void* x, void* y, void* workspace, size_t ws_bytes,
                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement: timing events around one step of the layer, in every layer
+ * of the iterations that follow.  For throughput accounting of a kernel as
+ * it runs inside real iterations (its neighbours, clocks and caches as in
+ * production), not needed to run the model.
+ * ---------------------------------------------------------------------- */
+enum {
+  ORCA_STEP_QKV = 0,        /* the QKV Linear with the K/V append */
+  ORCA_STEP_ATTENTION = 1,  /* split attention (every request, both phases) */
+  ORCA_STEP_OUT_PROJ = 2,   /* output projection + residual (not the LN after it,
+                               except fused into a split-K reduce) */
+  ORCA_STEP_FFN1 = 3,       /* FFN1 + GeLU */
+  ORCA_STEP_FFN2 = 4        /* FFN2 + residual (as ORCA_STEP_OUT_PROJ) */
+};
+
+/* Choose the step to time (-1: none).  The first call with a step creates
+ * two HIP timing events per layer, owned by the context; every later
+ * orca_iteration records them on its stream before and after that step of
+ * each layer.  ORCA_ERR_INVALID for an unknown step; ORCA_ERR_HIP if the
+ * events cannot be created (timing then stays off). */
+orca_status orca_time_step(orca_ctx* ctx, int32_t step);
+
+/* Per-layer milliseconds of the chosen step in the last iteration that ran
+ * with it, for layers 0 .. min(n, layers)-1, into host ms[].  Waits for that
+ * iteration to finish.  ORCA_ERR_INVALID if no step is chosen or no
+ * iteration has run since it was chosen. */
+orca_status orca_step_times(orca_ctx* ctx, float* ms, int32_t n);
 
 /* ------------------------------------------------------------------------
  * Single-step entry points: the kernels orca_iteration launches, one step

@@ -59,6 +59,10 @@ struct orca_ctx {
   bool ev_live[NSLOT] = {};
   int slot = 0;
   std::vector<std::pair<int64_t, int64_t>> ranges;   // scratch for validation
+  // timing of one step of every layer (orca_time_step): events [layer][2]
+  int probe_step = -1;
+  bool probe_recorded = false;
+  std::vector<hipEvent_t> probe_ev;
 
   size_t layer_pool_elems() const {
     return (size_t)desc.heads * (size_t)desc.kv_capacity * (size_t)(desc.hidden / desc.heads);
@@ -332,6 +336,10 @@ orca_status orca_create(const orca_model_desc* desc, const orca_layer_weights* l
 
 orca_status orca_destroy(orca_ctx* c) {
   if (!c) return ORCA_OK;
+  for (hipEvent_t e : c->probe_ev) {
+    (void)hipEventSynchronize(e);
+    (void)hipEventDestroy(e);
+  }
   for (int i = 0; i < NSLOT; ++i) {
     if (c->ev[i]) {
       (void)hipEventSynchronize(c->ev[i]);
@@ -390,6 +398,14 @@ orca_status orca_iteration(orca_ctx* c, const orca_req_desc* reqs, int32_t n_req
   void* gp = ws + c->off_gpart;
   const size_t gpb = c->gpart_bytes;
 
+  const bool probe = c->probe_step >= 0;
+  auto mark = [&](int l, int step, int end) -> hipError_t {
+    if (!probe || step != c->probe_step) return hipSuccess;
+    return hipEventRecord(c->probe_ev[2 * l + end], s);
+  };
+  auto probe_mid = [&](int l, int step) -> hipEvent_t {
+    return probe && step == c->probe_step ? c->probe_ev[2 * l + 1] : nullptr;
+  };
   HIP_TRY(launch_to_f32(dt, x, resid, int64_t(R) * H, s), "input conversion");
   // LN1 of layer 0 here; every later LayerNorm runs with the residual
   // Linear before it (one kernel with its split-K reduce when that applies)
@@ -399,25 +415,71 @@ orca_status orca_iteration(orca_ctx* c, const orca_req_desc* reqs, int32_t n_req
     const orca_layer_weights& w = c->layers[l];
     QkvDest qd{q, static_cast<char*>(c->k_pool) + pool * l, static_cast<char*>(c->v_pool) + pool * l,
                row_dst, H, H / d.heads, d.kv_capacity};
+    HIP_TRY(mark(l, ORCA_STEP_QKV, 0), "timing event");
     HIP_TRY(launch_linear(dt, EPI_QKV, a, w.w_qkv, w.b_qkv, nullptr, &qd, R, 3 * H, H, gp, gpb, s), "QKV");
+    HIP_TRY(mark(l, ORCA_STEP_QKV, 1), "timing event");
+    HIP_TRY(mark(l, ORCA_STEP_ATTENTION, 0), "timing event");
     st = run_attention(c, l, aa, q, o, s);
     if (st != ORCA_OK) return st;
+    HIP_TRY(mark(l, ORCA_STEP_ATTENTION, 1), "timing event");
+    HIP_TRY(mark(l, ORCA_STEP_OUT_PROJ, 0), "timing event");
     HIP_TRY(launch_linear_resid_ln(dt, o, w.w_o, w.b_o, resid, R, H, H, gp, gpb, w.ln2_g, w.ln2_b, a,
-                                   d.ln_eps, s),
+                                   d.ln_eps, s, probe_mid(l, ORCA_STEP_OUT_PROJ)),
             "output projection + LN2");
+    HIP_TRY(mark(l, ORCA_STEP_FFN1, 0), "timing event");
     HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_GELU, a, w.w_1, w.b_1, f, nullptr, R, F, H, gp, gpb, s), "FFN1");
+    HIP_TRY(mark(l, ORCA_STEP_FFN1, 1), "timing event");
+    HIP_TRY(mark(l, ORCA_STEP_FFN2, 0), "timing event");
     if (l + 1 < d.layers) {
       const orca_layer_weights& wn = c->layers[l + 1];
       HIP_TRY(launch_linear_resid_ln(dt, f, w.w_2, w.b_2, resid, R, H, F, gp, gpb, wn.ln1_g, wn.ln1_b,
-                                     a, d.ln_eps, s),
+                                     a, d.ln_eps, s, probe_mid(l, ORCA_STEP_FFN2)),
               "FFN2 + next LN1");
     } else {
       HIP_TRY(launch_linear(dt, ORCA_EPI_BIAS_RESID, f, w.w_2, w.b_2, resid, nullptr, R, H, F, gp, gpb,
                             s),
               "FFN2");
+      HIP_TRY(mark(l, ORCA_STEP_FFN2, 1), "timing event");
     }
   }
+  if (probe) c->probe_recorded = true;
   HIP_TRY(launch_from_f32(dt, resid, y, int64_t(R) * H, s), "output conversion");
+  return ORCA_OK;
+}
+
+// ------------------------------------------------------------ step timing
+
+orca_status orca_time_step(orca_ctx* c, int32_t step) {
+  clear_error();
+  ORCA_CHECK_ARG(c != nullptr, "NULL context");
+  ORCA_CHECK_ARG(step >= -1 && step <= ORCA_STEP_FFN2, "unknown step %d", step);
+  if (step >= 0 && c->probe_ev.empty()) {
+    c->probe_ev.assign(2 * size_t(c->desc.layers), nullptr);
+    for (hipEvent_t& e : c->probe_ev) {
+      const hipError_t r = hipEventCreate(&e);
+      if (r != hipSuccess) {
+        for (hipEvent_t& f : c->probe_ev)
+          if (f) (void)hipEventDestroy(f);
+        c->probe_ev.clear();
+        return hip_fail(r, "orca_time_step");
+      }
+    }
+  }
+  c->probe_step = step;
+  c->probe_recorded = false;
+  return ORCA_OK;
+}
+
+orca_status orca_step_times(orca_ctx* c, float* ms, int32_t n) {
+  clear_error();
+  ORCA_CHECK_ARG(c != nullptr && (ms != nullptr || n == 0), "NULL argument");
+  ORCA_CHECK_ARG(c->probe_step >= 0 && c->probe_recorded,
+                 "no iteration has run since a step was chosen for timing");
+  const int layers = std::min<int>(n, c->desc.layers);
+  HIP_TRY(hipEventSynchronize(c->probe_ev[2 * size_t(c->desc.layers) - 1]), "timing wait");
+  for (int l = 0; l < layers; ++l)
+    HIP_TRY(hipEventElapsedTime(&ms[l], c->probe_ev[2 * l], c->probe_ev[2 * l + 1]),
+            "timing read");
   return ORCA_OK;
 }
 

@@ -1414,14 +1414,14 @@ hipError_t launch_linear(int dtype, int epilogue, const void* a, const void* w, 
 hipError_t launch_linear_resid_ln(int dtype, const void* a, const void* w, const void* bias,
                                   float* resid, int m, int n, int k, void* ws, size_t ws_bytes,
                                   const void* ln_g, const void* ln_b, void* ln_out, float eps,
-                                  hipStream_t s) {
+                                  hipStream_t s, hipEvent_t after_gemm) {
   if (m == 0) return hipSuccess;
   SplitPlan sp{};
   if (dtype == ORCA_BF16 && plan_gemm(m, n, k, sp) == 10 && ws &&
       ws_bytes >= (size_t)sp.splits * m * n * sizeof(float)) {
     float* part = static_cast<float*>(ws);
     launch_partials(sp, a, w, part, m, n, k, s);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = after_gemm ? hipEventRecord(after_gemm, s) : hipGetLastError();
     if (e != hipSuccess) return e;
     const hipError_t f =
         launch_reduce_resid_ln(part, sp.splits, bias, resid, m, n, ln_g, ln_b, ln_out, eps, s);
@@ -1437,6 +1437,10 @@ hipError_t launch_linear_resid_ln(int dtype, const void* a, const void* w, const
     const hipError_t e = launch_linear(dtype, ORCA_EPI_BIAS_RESID, a, w, bias, resid, nullptr, m,
                                        n, k, ws, ws_bytes, s);
     if (e != hipSuccess) return e;
+    if (after_gemm) {
+      const hipError_t f = hipEventRecord(after_gemm, s);
+      if (f != hipSuccess) return f;
+    }
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -50,11 +50,12 @@ hipError_t launch_linear(int dtype, int epilogue, const void* a, const void* w, 
                          size_t ws_bytes, hipStream_t s);
 // The residual-epilogue Linear (out is the fp32 residual [m][n]) followed
 // by the LayerNorm of the new residual into ln_out; on the split-K path the
-// two share one kernel after the partial GEMM.
+// two share one kernel after the partial GEMM.  `after_gemm`, when not
+// NULL, is recorded on `s` after the GEMM's launches and before the rest.
 hipError_t launch_linear_resid_ln(int dtype, const void* a, const void* w, const void* bias,
                                   float* resid, int m, int n, int k, void* ws, size_t ws_bytes,
                                   const void* ln_g, const void* ln_b, void* ln_out, float eps,
-                                  hipStream_t s);
+                                  hipStream_t s, hipEvent_t after_gemm = nullptr);
 
 // ---- Attention (attn.hip) --------------------------------------------------
 // Device request record: same layout as orca_req_desc.

@@ -26,6 +26,7 @@ ORCA_F32, ORCA_BF16 = 0, 1
 ORCA_INITIATION, ORCA_INCREMENT = 0, 1
 ORCA_EPI_BIAS, ORCA_EPI_BIAS_GELU, ORCA_EPI_BIAS_RESID = 0, 1, 2
 ORCA_POLICY_ITERATION, ORCA_POLICY_STATIC, ORCA_POLICY_CHUNKED = 0, 1, 2
+ORCA_STEP_QKV, ORCA_STEP_ATTENTION, ORCA_STEP_OUT_PROJ, ORCA_STEP_FFN1, ORCA_STEP_FFN2 = range(5)
 
 LAYER_KEYS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
               "ln2_g", "ln2_b", "w_1", "b_1", "w_2", "b_2")
@@ -75,6 +76,8 @@ def _declare(lib):
         "orca_destroy": (c_int32, [V]),
         "orca_workspace_bytes": (S, [V]),
         "orca_iteration": (c_int32, [V, POINTER(orca_req_desc), I32, V, V, V, S, V]),
+        "orca_time_step": (c_int32, [V, I32]),
+        "orca_step_times": (c_int32, [V, POINTER(c_float), I32]),
         "orca_op_layernorm": (c_int32, [I32, V, V, V, V, I32, I32, c_float, V]),
         "orca_op_linear_workspace_bytes": (S, [I32, I32, I32, I32]),
         "orca_op_linear_variant": (I32, [I32, I32, I32, I32]),
@@ -225,6 +228,16 @@ def orca_iteration(ctx: int, reqs: Sequence, x, y, workspace, ws_bytes: int,
     arr = req_array(reqs)
     _check(load().orca_iteration(ctx, arr, len(reqs), ptr(x), ptr(y), ptr(workspace), ws_bytes,
                                  stream_handle(stream)), "orca_iteration")
+
+
+def orca_time_step(ctx: int, step: int) -> None:
+    _check(load().orca_time_step(ctx, step), "orca_time_step")
+
+
+def orca_step_times(ctx: int, layers: int) -> List[float]:
+    ms = (c_float * max(layers, 1))()
+    _check(load().orca_step_times(ctx, ms, layers), "orca_step_times")
+    return [ms[i] for i in range(layers)]
 
 
 def orca_op_layernorm(dtype: int, x, gamma, beta, out, rows: int, hidden: int, eps: float,

@@ -37,15 +37,29 @@ def check_against_oracle(work, seed=0, hin=None):
                                          hin.x.astype(np.float64), f64_caches(hin.caches),
                                          work.heads, work.eps)
         errs = {"y": rel_err(y, yr)}
+        # each request judged against its own magnitude as well: its output
+        # rows, and its appended K and V rows at every layer
+        per_req = {}
+        offs = work.q_offset
+        for i in range(work.n_reqs):
+            rows = slice(offs[i], offs[i] + work.q_len[i])
+            per_req[("y", i)] = rel_err(y[rows], yr[rows])
         for l in range(work.layers):
             ks, vs, kr, vr = [], [], [], []
             for i in range(work.n_reqs):
                 k, v = model.cache_rows(l, i, work.kv_len[i], work.kv_len[i] + work.q_len[i])
                 ks.append(k); vs.append(v); kr.append(app[l][i][0]); vr.append(app[l][i][1])
+                per_req[(f"k{l}", i)] = rel_err(k, app[l][i][0])
+                per_req[(f"v{l}", i)] = rel_err(v, app[l][i][1])
             errs[f"k{l}"] = rel_err(np.concatenate(ks), np.concatenate(kr))
             errs[f"v{l}"] = rel_err(np.concatenate(vs), np.concatenate(vr))
-        print(work.name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+        worst = max(per_req, key=per_req.get)
+        print(work.name, {k: f"{v:.2e}" for k, v in errs.items()},
+              f"worst per request: {worst[0]} of request {worst[1]} {per_req[worst]:.2e}",
+              flush=True)
         for k, e in errs.items():
+            assert e < TOL[work.dtype], (k, e)
+        for k, e in per_req.items():
             assert e < TOL[work.dtype], (k, e)
         return y, model
     except Exception:
@@ -209,3 +223,33 @@ def test_wide_rows_on_the_split_path(layers, hidden, heads):
                                  [1] * 12 + [5], [30] * 6 + [200] * 6 + [0])
     _, m = check_against_oracle(work, seed=hidden)
     m.close()
+
+
+def test_step_timing_events():
+    """The timing hook records per-layer times of the chosen step and leaves
+    the iteration's results bit for bit unchanged."""
+    print("case step timing", flush=True)
+    work = synth.custom_workload(3, 512, 8, 1024, "bf16", [1, 70, 1], [40, 0, 300])
+    hin = synth.host_inputs(work, 11)
+    model = DeviceModel(work, host=hin, device=DEV)
+    try:
+        with pytest.raises(L.OrcaError) as e:
+            L.orca_step_times(model.ctx, work.layers)       # nothing chosen yet
+        assert e.value.status == L.ORCA_ERR_INVALID
+        with pytest.raises(L.OrcaError):
+            L.orca_time_step(model.ctx, 5)
+        base = run_gpu(model, work, hin.x)
+        for step in (L.ORCA_STEP_QKV, L.ORCA_STEP_ATTENTION, L.ORCA_STEP_OUT_PROJ,
+                     L.ORCA_STEP_FFN1, L.ORCA_STEP_FFN2):
+            L.orca_time_step(model.ctx, step)
+            with pytest.raises(L.OrcaError):
+                L.orca_step_times(model.ctx, work.layers)   # no iteration since
+            y = run_gpu(model, work, hin.x)
+            ms = L.orca_step_times(model.ctx, work.layers)
+            assert len(ms) == work.layers and all(0.0 < t < 1000.0 for t in ms), (step, ms)
+            assert np.array_equal(y.view(np.uint32), base.view(np.uint32)), step
+        L.orca_time_step(model.ctx, -1)
+        assert np.array_equal(run_gpu(model, work, hin.x).view(np.uint32),
+                              base.view(np.uint32))
+    finally:
+        model.close()
