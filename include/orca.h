@@ -268,6 +268,26 @@ orca_status orca_op_linear(int32_t dtype, int32_t epilogue, const void* a, const
                            const void* bias, void* out, int32_t m, int32_t n, int32_t k,
                            void* workspace, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc): orca_op_linear
+ * without the workspace argument.  Its split-K partial sums live in a static
+ * device buffer of ORCA_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends (its address is looked up on
+ * the first call on each device).  The caller still passes the inputs and
+ * the output.  Same kernels, plan and results as orca_op_linear given
+ * orca_op_linear_workspace_bytes of workspace.  Calls that overlap on one
+ * GPU (two streams or two threads) race on the buffer: serialise them.  No
+ * part of the buffer needs to start at zero (a call writes every partial
+ * sum it reads), and the last call's contents stay in it.
+ * ORCA_ERR_UNSUPPORTED when the problem's split-K plan needs more than
+ * ORCA_NOALLOC_SCRATCH_BYTES (orca_op_linear_workspace_bytes(dtype, m, n, k)
+ * tells in advance); otherwise as orca_op_linear.  Allocates no memory and
+ * calls no allocating routine. */
+#define ORCA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+orca_status orca_op_linear_noalloc(int32_t dtype, int32_t epilogue, const void* a, const void* w,
+                                   const void* bias, void* out, int32_t m, int32_t n, int32_t k,
+                                   void* stream);
+
 /* The fused QKV projection with the K/V manager's append: for every row m,
  * [q|k|v] = a[m] W_qkv^T + b_qkv; q goes to q_out[m][0..H-1]; k and v of
  * head h go to k_pool_l[h][row_dst[m]][..] and v_pool_l[h][row_dst[m]][..].

@@ -30,11 +30,13 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "device.h"
 #include "kernels.h"
 #include "orca.h"
+#include "status.h"
 
 namespace orca {
 
@@ -1448,3 +1450,69 @@ hipError_t launch_linear_resid_ln(int dtype, const void* a, const void* w, const
 }
 
 }  // namespace orca
+
+// ------------------------------------------------- allocation-free Linear
+
+// The split-K partial sums of orca_op_linear_noalloc.  Every GPU the library
+// runs on holds its own copy until the process ends.  In host code the name
+// stands for no device address: the address comes from hipGetSymbolAddress
+// with the device current, once per device.
+static __device__ __align__(256) unsigned char scratch[ORCA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[MAX_DEVICES] = {};
+
+// Address of the current device's copy of `scratch`.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" orca_status orca_op_linear_noalloc(int32_t dtype, int32_t epilogue, const void* a,
+                                              const void* w, const void* bias, void* out,
+                                              int32_t m, int32_t n, int32_t k, void* stream) {
+  orca::clear_error();
+  ORCA_CHECK_ARG(dtype == ORCA_F32 || dtype == ORCA_BF16, "unknown dtype %d", dtype);
+  ORCA_CHECK_ARG(epilogue >= ORCA_EPI_BIAS && epilogue <= ORCA_EPI_BIAS_RESID,
+                 "unknown epilogue %d", epilogue);
+  ORCA_CHECK_ARG(m >= 0 && n >= 64 && k >= 64, "shape m %d n %d k %d", m, n, k);
+  if (n % 64 || k % 64) {
+    orca::set_error("unsupported shape: n %d and k %d must be multiples of 64", n, k);
+    return ORCA_ERR_UNSUPPORTED;
+  }
+  ORCA_CHECK_ARG(m == 0 || (a && w && bias && out), "NULL argument");
+  if (m == 0) return ORCA_OK;
+  const size_t need = orca::linear_workspace_bytes(dtype, m, n, k);
+  if (need > ORCA_NOALLOC_SCRATCH_BYTES) {
+    orca::set_error("the split-K partial sums of m %d n %d k %d need %zu bytes; the static "
+                    "scratch holds %zu (use orca_op_linear with a workspace)",
+                    m, n, k, need, (size_t)ORCA_NOALLOC_SCRATCH_BYTES);
+    return ORCA_ERR_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e == hipSuccess)
+    e = orca::launch_linear(dtype, epilogue, a, w, bias, out, nullptr, m, n, k, ws,
+                            ORCA_NOALLOC_SCRATCH_BYTES, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    orca::set_error("orca_op_linear_noalloc: %s", hipGetErrorString(e));
+    return ORCA_ERR_HIP;
+  }
+  return ORCA_OK;
+}

@@ -82,6 +82,7 @@ def _declare(lib):
         "orca_op_linear_workspace_bytes": (S, [I32, I32, I32, I32]),
         "orca_op_linear_variant": (I32, [I32, I32, I32, I32]),
         "orca_op_linear": (c_int32, [I32, I32, V, V, V, V, I32, I32, I32, V, S, V]),
+        "orca_op_linear_noalloc": (c_int32, [I32, I32, V, V, V, V, I32, I32, I32, V]),
         "orca_op_qkv": (c_int32, [I32, V, V, V, V, V, V, V, I32, I32, I32, I64, V, S, V]),
         "orca_op_attention": (c_int32, [V, I32, POINTER(orca_req_desc), I32, V, V, V, S, V]),
         "orca_sched_create": (c_int32, [V, I32, I32, I32, POINTER(V)]),
@@ -259,6 +260,16 @@ def orca_op_linear(dtype: int, epilogue: int, a, w, bias, out, m: int, n: int, k
     _check(load().orca_op_linear(dtype, epilogue, ptr(a), ptr(w), ptr(bias), ptr(out), m, n, k,
                                  ptr(workspace), ws_bytes, stream_handle(stream)),
            "orca_op_linear")
+
+
+ORCA_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def orca_op_linear_noalloc(dtype: int, epilogue: int, a, w, bias, out, m: int, n: int, k: int,
+                           stream=None) -> None:
+    _check(load().orca_op_linear_noalloc(dtype, epilogue, ptr(a), ptr(w), ptr(bias), ptr(out),
+                                         m, n, k, stream_handle(stream)),
+           "orca_op_linear_noalloc")
 
 
 def orca_op_qkv(dtype: int, a, w_qkv, b_qkv, q_out, k_pool_l, v_pool_l, row_dst, m: int,

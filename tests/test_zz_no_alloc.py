@@ -1,0 +1,82 @@
+"""orca_op_linear_noalloc (the Linear for callers that cannot allocate device
+memory: its split-K partial sums live in the library's static per-GPU
+buffer) against orca_op_linear given a workspace, through the C ABI.
+
+Same kernels and launch plan on both sides, so the outputs must agree bit
+for bit; the oracle's bar is checked as well.  Two calls in a row, the
+second on a smaller input, and the size limit's error.
+"""
+import numpy as np
+import pytest
+
+from oracle import model as om
+from orca_selective_iteration_amd import lib as L
+from orca_selective_iteration_amd import synth
+from tests.util import TOL, rel_err
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _inputs(rng, m, n, k, epi):
+    def bf(shape, scale):
+        return synth.round_to_bf16((scale * rng.standard_normal(shape)).astype(np.float32))
+    a, w, b = bf((m, k), 1.0), bf((n, k), 0.02 * 32 / np.sqrt(k)), bf(n, 0.02)
+    init = rng.standard_normal((m, n)).astype(np.float32) if epi == L.ORCA_EPI_BIAS_RESID else None
+    ref = om.linear(a.astype(np.float64), w.astype(np.float64), b.astype(np.float64))
+    if epi == L.ORCA_EPI_BIAS_GELU:
+        ref = om.gelu_tanh(ref)
+    if init is not None:
+        ref = init.astype(np.float64) + ref
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV, torch.bfloat16)
+    return t(a), t(w), t(b), init, ref
+
+
+def _out(m, n, epi, init):
+    if init is not None:
+        return torch.from_numpy(init).to(DEV)
+    return torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+
+
+def _bits(t):
+    torch.cuda.synchronize()
+    return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)).cpu().numpy()
+
+
+@pytest.mark.parametrize("epi", [L.ORCA_EPI_BIAS_GELU, L.ORCA_EPI_BIAS_RESID, L.ORCA_EPI_BIAS])
+def test_noalloc_matches_the_workspace_path(epi):
+    # 13B-shaped few-rows Linears (the split-K path: fp32 partial planes in
+    # the static buffer), then a smaller call reusing the buffer, then a
+    # tiled shape that needs no scratch
+    for m, n, k in ((64, 5120, 5120), (16, 2560, 5120), (40, 20480, 5120), (520, 768, 1024)):
+        print(f"case noalloc epi={epi} m={m} n={n} k={k}", flush=True)
+        nb = L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k)
+        assert nb <= L.ORCA_NOALLOC_SCRATCH_BYTES
+        if (m, n, k) != (520, 768, 1024):
+            assert nb > 0, "expected the split-K path"
+        rng = np.random.default_rng(m + n + k + epi)
+        a, w, b, init, ref = _inputs(rng, m, n, k, epi)
+        out_ws = _out(m, n, epi, init)
+        ws = torch.full((max(nb, 4) // 4,), float("nan"), dtype=torch.float32, device=DEV)
+        L.orca_op_linear(L.ORCA_BF16, epi, a, w, b, out_ws, m, n, k, ws, nb)
+        out_na = _out(m, n, epi, init)
+        L.orca_op_linear_noalloc(L.ORCA_BF16, epi, a, w, b, out_na, m, n, k)
+        got_ws, got_na = _bits(out_ws), _bits(out_na)
+        assert np.array_equal(got_ws, got_na), (m, n, k)
+        assert rel_err(out_na.float().cpu().numpy(), ref) < TOL["bf16"]
+
+
+def test_noalloc_rejects_problems_past_its_buffer():
+    m, n, k = 300, 15360, 5120          # split-K partials of 35 MiB
+    assert L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k) > L.ORCA_NOALLOC_SCRATCH_BYTES
+    a = torch.zeros((m, k), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((n, k), dtype=torch.bfloat16, device=DEV)
+    b = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    out = torch.full((m, n), 5.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(L.OrcaError) as e:
+        L.orca_op_linear_noalloc(L.ORCA_BF16, L.ORCA_EPI_BIAS, a, w, b, out, m, n, k)
+    assert e.value.status == L.ORCA_ERR_UNSUPPORTED
+    assert "static" in str(e.value)
+    torch.cuda.synchronize()
+    assert bool((out == 5.0).all())
