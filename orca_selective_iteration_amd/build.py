@@ -81,6 +81,28 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(BUILD, "liborca_host_san.so")
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=all"]
+
+
+def build_host_sanitized() -> str:
+    """The host-only part of the library (status, K/V allocator, scheduler)
+    built with AddressSanitizer and UndefinedBehaviorSanitizer, for running
+    the host tests against it (ORCA_LIB / ORCA_HOST_ONLY, see lib.py).  CPU
+    code only: g++, no HIP source.  Returns the library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    gxx = shutil.which("g++") or "g++"
+    objs = []
+    for src in CPP_SOURCES:
+        obj = os.path.join(BUILD, src + ".san.o")
+        _run([gxx, *SAN_FLAGS, "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC, "-c",
+              os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    _run([gxx, *SAN_FLAGS, "-shared", "-o", SAN_LIB, *objs])
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)

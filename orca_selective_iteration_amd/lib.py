@@ -18,7 +18,10 @@ from typing import Iterable, List, Optional, Sequence
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-LIB_PATH = os.path.join(PKG, "liborca.so")
+# ORCA_LIB names another build of the library (the sanitized host-only
+# build); ORCA_HOST_ONLY=1 accepts one that has only the host entry points
+LIB_PATH = os.environ.get("ORCA_LIB") or os.path.join(PKG, "liborca.so")
+HOST_ONLY = os.environ.get("ORCA_HOST_ONLY") == "1"
 HEADER = os.path.join(ROOT, "include", "orca.h")
 
 ORCA_OK, ORCA_ERR_INVALID, ORCA_ERR_NOSPACE, ORCA_ERR_HIP, ORCA_ERR_UNSUPPORTED = range(5)
@@ -97,18 +100,35 @@ def _declare(lib):
         "orca_sched_used": (I64, [V]),
     }
     for name, (res, args) in sig.items():
+        if HOST_ONLY and not hasattr(lib, name):
+            continue
         f = getattr(lib, name)
         f.restype = res
         f.argtypes = args
 
 
+def _stale() -> bool:
+    """True when a source is newer than the built library."""
+    built = os.path.getmtime(LIB_PATH)
+    srcs = [os.path.join(PKG, "csrc", f) for f in os.listdir(os.path.join(PKG, "csrc"))]
+    return any(os.path.getmtime(f) > built for f in srcs + [HEADER] if os.path.exists(f))
+
+
 def load():
-    """The loaded library (built in-tree first if it does not exist)."""
+    """The loaded library.  If it has not been built yet it is built
+    in-tree first; a build older than its sources is loaded with a warning
+    (rebuild: python -m orca_selective_iteration_amd.build)."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
+            if os.environ.get("ORCA_LIB"):
+                raise OSError(f"ORCA_LIB names a missing library: {LIB_PATH}")
             from .build import build
             build()
+        elif not os.environ.get("ORCA_LIB") and _stale():
+            import warnings
+            warnings.warn(f"{LIB_PATH} is older than its sources; rebuild with "
+                          f"python -m orca_selective_iteration_amd.build", stacklevel=2)
         lib = ctypes.CDLL(LIB_PATH)
         _declare(lib)
         _lib = lib

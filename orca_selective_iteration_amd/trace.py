@@ -25,7 +25,7 @@ import argparse
 import json
 import sys
 import time
-from typing import List, Optional
+from typing import Dict, List, Optional
 
 import numpy as np
 
@@ -74,7 +74,8 @@ class TraceEngine:
         self.y = torch.empty_like(self.x)
 
     def run(self, requests: List[synth.TraceRequest], max_batch: int, token_budget: int,
-            policy: int, log=None, max_wall: float = 1e9, depth: int = 1) -> dict:
+            policy: int, log=None, max_wall: float = 1e9, depth: int = 1,
+            cancels: Optional[Dict[int, List[int]]] = None, record: bool = False) -> dict:
         """Serve `requests` under `policy`.  depth = iterations the loop keeps
         queued on the stream: 1 waits for every iteration before the next
         scheduling step; 2 or more schedule and launch iteration k+1 while k
@@ -84,7 +85,14 @@ class TraceEngine:
         return; unpurerationalist.github.io ORCA notes 4.1: a controller
         hands its kernels to the GPU and goes on without waiting).  The step
         clock is the host clock either way; an iteration's end time is read
-        from a timing event."""
+        from a timing event.
+
+        cancels: {scheduling call index: request ids} withdrawn just before
+        that call (garden.houmin.site/infra/orca 3.1.1: a cancelled request
+        should leave promptly and free its memory); a withdrawal the
+        scheduler refuses (already released) is logged as refused.
+        record: also return every iteration's descriptors and a copy of its
+        output rows (taken on the stream, in order, without waiting)."""
         import torch
         from collections import deque
         log = log or (lambda *a: None)
@@ -101,11 +109,21 @@ class TraceEngine:
             now = 0.0
             steps: List[tuple] = []      # non-empty iterations: (now, ids)
             calls: List[tuple] = []      # every scheduling step, for replay
+            batches: List[tuple] = []    # record: descriptors of each iteration
+            outputs: List = []           # record: output rows of each iteration
+            withdrawn: List[tuple] = []  # (call index, id, accepted)
+            cancels = cancels or {}
             ends: List = []              # timing event after each iteration
             flight = deque()
             iters = rows = busy = 0
             last_print = t0
             while not L.orca_sched_idle(s):
+                for rid in cancels.get(len(calls), ()):
+                    try:
+                        L.orca_sched_cancel(s, rid)
+                        withdrawn.append((len(calls), rid, True))
+                    except L.OrcaError:
+                        withdrawn.append((len(calls), rid, False))
                 descs, ids = L.orca_sched_step(s, now, max_batch)
                 calls.append((now, tuple(ids)))
                 if not descs:
@@ -122,6 +140,10 @@ class TraceEngine:
                     continue
                 n_rows = descs[-1].q_offset + descs[-1].q_len
                 L.orca_iteration(self.ctx, descs, self.x, self.y, self.ws, self.ws_bytes, stream)
+                if record:
+                    batches.append(tuple((d.q_offset, d.q_len, d.kv_len, d.phase, d.kv_base)
+                                         for d in descs))
+                    outputs.append(self.y[:n_rows].clone())
                 ev = torch.cuda.Event(enable_timing=True)
                 ev.record(stream)
                 ends.append(ev)
@@ -144,8 +166,14 @@ class TraceEngine:
             # per-request latency: time the iteration holding its last token ended
             iter_end = [start.elapsed_time(e) * 1e-3 for e in ends]
             lats = []
+            gen = 0
+            info = {}
             for r in requests:
-                _, fin, rel = L.orca_sched_request_info(s, r.id)
+                adm, fin, rel = L.orca_sched_request_info(s, r.id)
+                info[r.id] = (adm, fin, rel)
+                if fin < 0:
+                    continue          # withdrawn before its last token
+                gen += r.out_len
                 if policy == L.ORCA_POLICY_STATIC:
                     # request-level: the response leaves with the whole batch,
                     # after the iteration before the step that released it
@@ -153,12 +181,11 @@ class TraceEngine:
                 else:
                     t_end = iter_end[fin]
                 lats.append(t_end - r.arrival)
-            gen = sum(r.out_len for r in requests)
-            lats = np.array(lats)
+            lats = np.array(lats) if lats else np.zeros(1)
             return {
                 "policy": POLICY_NAMES[policy], "depth": depth,
                 "wall_s": round(wall, 3), "iterations": iters, "rows_processed": rows,
-                "generated_tokens": gen,
+                "generated_tokens": gen,      # of the requests that finished
                 "generated_tokens_per_s": round(gen / wall, 1),
                 "processed_tokens_per_s": round(rows / wall, 1),
                 "requests_per_s": round(len(requests) / wall, 3),
@@ -168,17 +195,30 @@ class TraceEngine:
                               "p99": round(float(np.percentile(lats, 99)), 3)},
                 "steps": steps,
                 "calls": calls,
+                "cancelled": withdrawn,
+                "request_info": info,         # id -> (admitted, finished, released)
+                "batches": batches if record else None,
+                "outputs": outputs if record else None,
             }
         finally:
             L.orca_sched_destroy(s)
 
     def close(self):
+        """Destroys the context and the allocator and drops the device
+        tensors (weights, pools, workspace), so their memory can be reused."""
         if self.ctx:
             L.orca_destroy(self.ctx)
             self.ctx = None
         if self.kv:
             L.orca_kv_destroy(self.kv)
             self.kv = None
+        self.weights = []
+        self.k_pool = self.v_pool = self.ws = self.x = self.y = None
+        try:
+            import torch
+            torch.cuda.empty_cache()
+        except Exception:
+            pass
 
 
 def main(argv=None):
@@ -216,7 +256,8 @@ def main(argv=None):
             log(f"policy {POLICY_NAMES[pol]}: {a.requests} requests at {a.rate}/s")
             res = eng.run(reqs, a.max_batch, a.token_budget, pol, log=log, max_wall=a.max_wall,
                           depth=a.depth)
-            res.pop("steps")
+            for k in ("steps", "batches", "outputs", "request_info"):
+                res.pop(k)
             calls = res.pop("calls")
             log(json.dumps(res))
             res["log"] = calls if a.log else None
