@@ -201,8 +201,9 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 // softmax max / sum need one cross-lane step (lane ^ 32).  The probabilities
 // feed O^T = V^T P^T straight from the score registers: the keys of the
 // PV MFMA's k-dimension are taken in the order in which the score tile
-// left them in the lanes (an order the V^T fragment reads follow), so P
-// never moves between lanes.  Online softmax in base 2 with a running max
+// left them in the lanes, and V^T stores the keys of every 16-key group in
+// that order (keys 4-7 and 8-11 swapped), so a lane's eight keys are one
+// 16-byte LDS read and P never moves between lanes.  Online softmax in base 2 with a running max
 // and sum per query; the output tile is transposed through LDS so the
 // [sum L, H] rows are written with 16-byte stores.
 template <int D>
@@ -262,6 +263,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   typedef uint32_t Stage __attribute__((ext_vector_type(4 * NL)));
   Stage kreg, vreg;
   const int vkey = tid & 63;
+  // V^T column of key pair (vkey & ~1): bits 2 and 3 of the key swapped
+  // inside its 16-key group, the order in which a lane's P^T fragment holds
+  // its keys (4 half + 0..3, then 8 + 4 half + 0..3), so the lane's eight
+  // keys are one 16-byte read
+  const int vcol = (vkey & ~15) | (vkey & 2) | ((vkey & 4) << 1) | ((vkey & 8) >> 1);
   // byte selectors of v_perm_b32 (bytes 0-3: second operand, 4-7: first):
   // even key lanes take (own.lo16, neighbour.lo16), odd ones
   // (neighbour.hi16, own.hi16)
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
         const uint32_t wv = vreg[4 * i + j];                                                 \
         const uint32_t nb =                                                                  \
             (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wv, 0xB1, 0xF, 0xF, false);       \
-        *reinterpret_cast<uint32_t*>(&stV[(vch * 8 + 2 * j + (vkey & 1)) * VLD + (vkey & ~1)]) = \
+        *reinterpret_cast<uint32_t*>(&stV[(vch * 8 + 2 * j + (vkey & 1)) * VLD + vcol]) =    \
             __builtin_amdgcn_perm(nb, wv, vsel);                                             \
       }                                                                                      \
     }                                                                                        \
@@ -332,12 +338,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     // causal mask, only on blocks reaching past the wave's first query or
     // the last key (wave-uniform test); running max on the raw scores, the
     // scale folded into the exponent below
-    float mx = NEG_BIG;
+    // (the max and the sum below run as four independent chains, not one
+    // 32-deep dependent chain per lane)
+    float mq[4] = {NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
     if (k0 + BKV - 1 <= qmin && k0 + BKV <= kend) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+        for (int r = 0; r < 16; ++r) mq[r & 3] = fmaxf(mq[r & 3], s[t][r]);
     } else {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -346,9 +354,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
           const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
           const bool vis = key <= qpos && key < kend;
           s[t][r] = vis ? s[t][r] : NEG_BIG;
-          mx = fmaxf(mx, s[t][r]);
+          mq[r & 3] = fmaxf(mq[r & 3], s[t][r]);
         }
     }
+    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // every query sees key 0 in the first block, so m_run is finite from
     // then on and a masked score's exponent is far below it (p = 0)
@@ -367,14 +376,16 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dm][r] *= corr;
     }
+    float lq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], sc, -m_new));
         s[t][r] = p;
-        l_run += p;
+        lq[r & 3] += p;
       }
+    l_run += (lq[0] + lq[1]) + (lq[2] + lq[3]);
     // O^T += V^T P^T, 16 keys per MFMA step
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -388,11 +399,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int dm = 0; dm < D / 32; ++dm) {
-        const uint16_t* vr = &sV[(dm * 32 + col) * VLD + 16 * st + 4 * half];
-        uint32_t vk[4];
-        *reinterpret_cast<uint2*>(&vk[0]) = *reinterpret_cast<const uint2*>(vr);
-        *reinterpret_cast<uint2*>(&vk[2]) = *reinterpret_cast<const uint2*>(vr + 8);
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vk);
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(
+            &sV[(dm * 32 + col) * VLD + 16 * st + 8 * half]);
         o[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[dm], 0, 0, 0);
       }
     }
