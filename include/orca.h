@@ -245,15 +245,18 @@ typedef enum {
 /* acc[m][n] = sum_k a[m][k] * w[n][k] on a device [m][k], w device [n][k],
  * bias device [n] (all `dtype`), then the epilogue.  m >= 0; n % 64 == 0 and
  * k % 64 == 0.  bf16 runs on the MFMA units.
- * workspace: device scratch owned by the caller, may be NULL.  For bf16
- * problems whose output tiles are too few to fill the GPU (chiefly batches of
- * few rows, made mostly of increment rows: the weights are streamed once
- * and the arithmetic is light) a split-K path runs when
- * ws_bytes >= orca_op_linear_workspace_bytes(dtype, m, n, k) > 0; it writes
- * fp32 partial sums there.  Otherwise the tiled path runs and the workspace
- * is not touched.  Both paths accumulate in fp32; only the summation order
- * differs.  orca_op_linear_workspace_bytes returns 0 where split-K does not
- * apply (fp32, or enough tiles). */
+ * workspace: device scratch owned by the caller, may be NULL.  With
+ * ws_bytes >= orca_op_linear_workspace_bytes(dtype, m, n, k) > 0 a bf16
+ * problem splits K where that pays, writing fp32 partial sums there:
+ *   - problems whose output tiles are too few to fill the GPU (chiefly
+ *     batches of few rows, made mostly of increment rows: the weights are
+ *     streamed once and the arithmetic is light) split every tile;
+ *   - large problems whose last round of tiles would leave more than half
+ *     the GPU idle split only that round's tiles (the rest run unsplit).
+ * Otherwise every tile runs over the whole of K and the workspace is not
+ * touched.  Every path accumulates in fp32; only the summation order
+ * differs.  orca_op_linear_workspace_bytes returns 0 where no split applies
+ * (fp32, or tiles that fill whole rounds). */
 size_t orca_op_linear_workspace_bytes(int32_t dtype, int32_t m, int32_t n, int32_t k);
 /* The kernel form orca_op_linear takes for this problem, without launching
  * anything (host only): the launch planner's choice after the fallbacks,
@@ -279,10 +282,11 @@ orca_status orca_op_linear(int32_t dtype, int32_t epilogue, const void* a, const
  * GPU (two streams or two threads) race on the buffer: serialise them.  No
  * part of the buffer needs to start at zero (a call writes every partial
  * sum it reads), and the last call's contents stay in it.
- * ORCA_ERR_UNSUPPORTED when the problem's split-K plan needs more than
- * ORCA_NOALLOC_SCRATCH_BYTES (orca_op_linear_workspace_bytes(dtype, m, n, k)
- * tells in advance); otherwise as orca_op_linear.  Allocates no memory and
- * calls no allocating routine. */
+ * ORCA_ERR_UNSUPPORTED when the few-rows split-K plan of the problem needs
+ * more than ORCA_NOALLOC_SCRATCH_BYTES (orca_op_linear_workspace_bytes(dtype,
+ * m, n, k) tells in advance); a tiled problem whose split-K tail would need
+ * more runs all its tiles over the whole of K instead.  Otherwise as
+ * orca_op_linear.  Allocates no memory and calls no allocating routine. */
 #define ORCA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 orca_status orca_op_linear_noalloc(int32_t dtype, int32_t epilogue, const void* a, const void* w,
                                    const void* bias, void* out, int32_t m, int32_t n, int32_t k,

@@ -132,6 +132,17 @@ __device__ __forceinline__ void tile_of(int logical, int tiles_m, int ntiles, in
   tn = idx / gm;
 }
 
+// Which tiles a four-wave launch covers.  A launch takes the logical tiles
+// tile_base .. tile_base + gridDim.x - 1 of a problem of ntiles tiles
+// (tile_of's order), each over K steps [y * kt_per_split, ...) for
+// blockIdx.y = y.  A data-parallel launch covers every tile over all of K;
+// the split-K tail of a hybrid launch covers the last n_tail tiles with K
+// split over grid.y, each split writing fp32 partial sums, tile-major.
+struct TileMap {
+  int tiles_m, ntiles, group;
+  int tile_base, kt_per_split, n_tail;
+};
+
 // Workgroup tile (WGM*32*TI) x (WGN*32*TJ): a WGM x WGN grid of waves, each
 // owning (32*TI) x (32*TJ) outputs as TI x TJ 32x32 MFMA accumulators.
 template <int WGM, int WGN, int TI, int TJ>
@@ -650,20 +661,25 @@ template <int EPI, int TJ>
 __global__ __launch_bounds__(W4_THREADS, 1)
 void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
                     const bf16* __restrict__ bias, EpiParams ep, int M, int N, int K,
-                    int tiles_m, int group_m) {
+                    TileMap map) {
   constexpr int TI = 4, BM = 256, BN = 64 * TJ;
   // 16-byte chunks per lane and K step: LA of A rows, then LB of W rows
   constexpr int LA = BM * 8 / W4_THREADS, LB = BN * 8 / W4_THREADS, NC = LA + LB;
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDK];
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int local = xcd_remap(blockIdx.x, gridDim.x);
+  const int logical = map.tile_base + local;
   int tm, tn;
-  tile_of(logical, tiles_m, gridDim.x, group_m, tm, tn);
+  tile_of(logical, map.tiles_m, map.ntiles, map.group, tm, tn);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int KT = K / BK;
+  // this workgroup's K steps: [k0, k0 + KT) (all of K outside a split tail)
+  const int k0 = blockIdx.y * map.kt_per_split;
+  const int KT = min(K / BK - k0, map.kt_per_split);
+  A += (size_t)k0 * BK;
+  W += (size_t)k0 * BK;
 
   // loads: lane tid moves chunk tid % 8 of rows tid / 8 + 32 i; byte
   // offsets from a uniform base keep each address to one register
@@ -685,10 +701,12 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
   // loads expect; num_records is the operand's size (the clamped offsets
   // never reach past it, and a read past it would return zeros)
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)A, (short)0, (int)(uint32_t)std::min<size_t>((size_t)M * K * 2, 0xffffffffu),
+      (void*)A, (short)0,
+      (int)(uint32_t)std::min<size_t>(((size_t)M * K - (size_t)k0 * BK) * 2, 0xffffffffu),
       0x00020000);
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)W, (short)0, (int)(uint32_t)std::min<size_t>((size_t)N * K * 2, 0xffffffffu),
+      (void*)W, (short)0,
+      (int)(uint32_t)std::min<size_t>(((size_t)N * K - (size_t)k0 * BK) * 2, 0xffffffffu),
       0x00020000);
 // chunk c of a stage: c < LA are A rows, the rest W rows
 #define ORCA_W4_LOAD(S, KS, C0, C1)                                                           \
@@ -794,8 +812,61 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
 #undef ORCA_W4_FRAGS
 #undef ORCA_W4_LOAD
 #undef ORCA_W4_STORE
-  store_wave_tile_t<EPI, TI, TJ>(acc, bias, ep, M, N, tm * BM + wm * 32 * TI,
-                                 tn * BN + wn * 32 * TJ, lane);
+  if constexpr (EPI == EPI_PARTIAL) {
+    // split tail: this split's sums of the tile, [split][tail tile][BM][BN]
+    ep.out = static_cast<float*>(ep.out) +
+             ((size_t)blockIdx.y * map.n_tail + local) * BM * BN;
+    ep.ldo = BN;
+    store_wave_tile_t<EPI, TI, TJ>(acc, bias, ep, M - tm * BM, N - tn * BN, wm * 32 * TI,
+                                   wn * 32 * TJ, lane);
+  } else {
+    store_wave_tile_t<EPI, TI, TJ>(acc, bias, ep, M, N, tm * BM + wm * 32 * TI,
+                                   tn * BN + wn * 32 * TJ, lane);
+  }
+}
+
+// The split-K tail of a hybrid four-wave launch: adds the splits' partial
+// sums of each tail tile, then the bias and the epilogue, four consecutive
+// columns per thread (they lie in one head of one block for the QKV
+// projection, as the head dim is a multiple of four).
+template <int EPI, int BN>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restrict__ part,
+                                                          int splits, TileMap map,
+                                                          const bf16* __restrict__ bias,
+                                                          EpiParams ep, int M, int N) {
+  constexpr int BM = 256, Q = BN / 4;
+  const int t = blockIdx.x;
+  int tm, tn;
+  tile_of(map.tile_base + t, map.tiles_m, map.ntiles, map.group, tm, tn);
+  const size_t plane = (size_t)map.n_tail * BM * BN;
+  for (int idx = blockIdx.y * 256 + threadIdx.x; idx < BM * Q; idx += gridDim.y * 256) {
+    const int r = idx / Q, c = (idx - r * Q) * 4;
+    const int m = tm * BM + r, n = tn * BN + c;
+    if (m >= M || n >= N) continue;
+    const float* p = part + (size_t)t * BM * BN + (size_t)r * BN + c;
+    float4 v = *reinterpret_cast<const float4*>(p);
+    for (int sp = 1; sp < splits; ++sp) {
+      const float4 u = *reinterpret_cast<const float4*>(p + sp * plane);
+      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    }
+    const uint2 bw = *reinterpret_cast<const uint2*>(bias + n);
+    float o[4] = {v.x + bf16_lo(bw.x), v.y + bf16_hi(bw.x), v.z + bf16_lo(bw.y),
+                  v.w + bf16_hi(bw.y)};
+    if constexpr (EPI == ORCA_EPI_BIAS_RESID) {
+      float4* q = reinterpret_cast<float4*>(static_cast<float*>(ep.out) + (size_t)m * ep.ldo + n);
+      const float4 old = *q;
+      *q = make_float4(old.x + o[0], old.y + o[1], old.z + o[2], old.w + o[3]);
+    } else {
+      if constexpr (EPI == ORCA_EPI_BIAS_GELU) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = gelu_tanh(o[e]);
+      }
+      const EpiCol<bf16, EPI> col(ep, n);
+      const int slot = EPI == EPI_QKV ? ep.qkv.row_dst[m] : 0;
+      *reinterpret_cast<uint2*>(col.ptr + (size_t)(col.slot ? slot : m) * col.stride) =
+          make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    }
+  }
 }
 
 // --------------------------------- one wave per SIMD, operands DMA'd to LDS
@@ -1232,6 +1303,38 @@ static int raster_group(int tiles_m) {
   return env_int("ORCA_GEMM_GROUP", tiles_m >= 12 ? 8 : 0);
 }
 
+// Hybrid four-wave launch: when the last round of resident workgroups is at
+// most half full, the tiles of every full round run as usual and the last
+// round's n_tail tiles run with K split by 2-4 (each split an even number
+// of at least 16 K steps), so that round ends in a fraction of a tile's
+// time; their fp32 partial sums (n_tail * splits tiles) are added by
+// tail_reduce_kernel, which applies the epilogue.  On the 175B layer shape
+// at 3,698 rows: QKV 2,160 tiles = 8 rounds + 112 tiles (2 splits), FFN1
+// 2,880 = 11 rounds + 64 (4 splits).  ORCA_GEMM_TAIL=0 turns it off.
+struct TailPlan {
+  int n_dp, n_tail, splits, per;
+};
+static bool tail_plan(int tiles, int kt, TailPlan& t) {
+  if (!env_int("ORCA_GEMM_TAIL", 1)) return false;
+  const int rem = tiles % NUM_CU;
+  if (tiles < NUM_CU || rem == 0 || rem > NUM_CU / 2 || kt % 2) return false;
+  int sp = std::min(4, NUM_CU / rem);
+  while (sp > 1 && kt / sp < 16) --sp;
+  if (sp < 2) return false;
+  int per = (kt + sp - 1) / sp;
+  per += per & 1;
+  t.splits = (kt + per - 1) / per;
+  t.per = per;
+  t.n_tail = rem;
+  t.n_dp = tiles - rem;
+  return t.splits >= 2;
+}
+// the four-wave forms' tile count (bn: 256 or 192)
+static int w4_tiles(int m, int n, int bn) { return ((m + 255) / 256) * ((n + bn - 1) / bn); }
+static bool w4_ok(int m, int n, int k) {
+  return k >= 2 * BK && (k / BK) % 2 == 0 && (long)std::max(m, n) * k < (1L << 31);
+}
+
 // The launch for one bf16 problem: a tiled variant, or split-K (`split`
 // filled, variant 10).  ORCA_GEMM_VARIANT=<n> pins the variant.
 static int plan_gemm(int m, int n, int k, SplitPlan& split) {
@@ -1274,8 +1377,16 @@ int linear_plan_variant(int dtype, int m, int n, int k) {
 
 size_t linear_workspace_bytes(int dtype, int m, int n, int k) {
   SplitPlan p{};
-  if (dtype != ORCA_BF16 || m < 1 || plan_gemm(m, n, k, p) != 10) return 0;
-  return (size_t)p.splits * m * n * sizeof(float);
+  if (dtype != ORCA_BF16 || m < 1) return 0;
+  const int v = plan_gemm(m, n, k, p);
+  if (v == 10) return (size_t)p.splits * m * n * sizeof(float);
+  if ((v == 12 || v == 13) && w4_ok(m, n, k)) {
+    const int bn = v == 12 ? 256 : 192;
+    TailPlan t;
+    if (tail_plan(w4_tiles(m, n, bn), k / BK, t))
+      return (size_t)t.n_tail * t.splits * 256 * bn * sizeof(float);
+  }
+  return 0;
 }
 
 template <int WGM, int WGN, int TI, int TJ, bool STREAM_W = false>
@@ -1355,14 +1466,30 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
         [[fallthrough]];
       case 12:
       case 13:
-        if ((v == 12 || v == 13) && k >= 2 * BK && (k / BK) % 2 == 0 &&
-            (long)std::max(m, n) * k < (1L << 31)) {
+        if ((v == 12 || v == 13) && w4_ok(m, n, k)) {
           const int bn = v == 12 ? 256 : 192;
-          const int tiles_m = (m + 255) / 256, tiles_n = (n + bn - 1) / bn;
+          const int tiles_m = (m + 255) / 256, tiles = w4_tiles(m, n, bn);
+          TileMap map{tiles_m, tiles, raster_group(tiles_m), 0, k / BK, 0};
+          TailPlan t;
+          const bool tail = tail_plan(tiles, k / BK, t) &&
+                            ws && ws_bytes >= (size_t)t.n_tail * t.splits * 256 * bn * 4;
+          if (tail) map.ntiles = tiles;
           auto kern = v == 12 ? gemm_w4_kernel<EPI, 4> : gemm_w4_kernel<EPI, 3>;
-          hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(W4_THREADS), 0, s,
-                             (const bf16*)a, (const bf16*)w, (const bf16*)bias, ep, m, n, k,
-                             tiles_m, raster_group(tiles_m));
+          hipLaunchKernelGGL(kern, dim3(tail ? t.n_dp : tiles), dim3(W4_THREADS), 0, s,
+                             (const bf16*)a, (const bf16*)w, (const bf16*)bias, ep, m, n, k, map);
+          if (tail) {
+            TileMap tm{tiles_m, tiles, map.group, t.n_dp, t.per, t.n_tail};
+            EpiParams pp{};
+            pp.out = ws;
+            auto pk = v == 12 ? gemm_w4_kernel<EPI_PARTIAL, 4> : gemm_w4_kernel<EPI_PARTIAL, 3>;
+            hipLaunchKernelGGL(pk, dim3(t.n_tail, t.splits), dim3(W4_THREADS), 0, s,
+                               (const bf16*)a, (const bf16*)w, (const bf16*)bias, pp, m, n, k,
+                               tm);
+            auto rk = v == 12 ? tail_reduce_kernel<EPI, 256> : tail_reduce_kernel<EPI, 192>;
+            hipLaunchKernelGGL(rk, dim3(t.n_tail, 16), dim3(256), 0, s,
+                               static_cast<const float*>(ws), t.splits, tm, (const bf16*)bias,
+                               ep, m, n);
+          }
           break;
         }
         if (v == 13) {   // odd K steps or offsets past 2^31: the 256 x 192 form
@@ -1499,17 +1626,20 @@ extern "C" orca_status orca_op_linear_noalloc(int32_t dtype, int32_t epilogue, c
   ORCA_CHECK_ARG(m == 0 || (a && w && bias && out), "NULL argument");
   if (m == 0) return ORCA_OK;
   const size_t need = orca::linear_workspace_bytes(dtype, m, n, k);
-  if (need > ORCA_NOALLOC_SCRATCH_BYTES) {
+  const bool few_rows = orca::linear_plan_variant(dtype, m, n, k) == 10;
+  if (need > ORCA_NOALLOC_SCRATCH_BYTES && few_rows) {
     orca::set_error("the split-K partial sums of m %d n %d k %d need %zu bytes; the static "
                     "scratch holds %zu (use orca_op_linear with a workspace)",
                     m, n, k, need, (size_t)ORCA_NOALLOC_SCRATCH_BYTES);
     return ORCA_ERR_UNSUPPORTED;
   }
+  // a tiled problem whose split tail would not fit runs without it
   void* ws = nullptr;
-  hipError_t e = scratch_address(&ws);
+  hipError_t e = need > ORCA_NOALLOC_SCRATCH_BYTES ? hipSuccess : scratch_address(&ws);
   if (e == hipSuccess)
     e = orca::launch_linear(dtype, epilogue, a, w, bias, out, nullptr, m, n, k, ws,
-                            ORCA_NOALLOC_SCRATCH_BYTES, static_cast<hipStream_t>(stream));
+                            ws ? ORCA_NOALLOC_SCRATCH_BYTES : 0,
+                            static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     orca::set_error("orca_op_linear_noalloc: %s", hipGetErrorString(e));
     return ORCA_ERR_HIP;

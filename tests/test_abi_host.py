@@ -329,3 +329,26 @@ def test_planner_variant_pin_and_rejects(monkeypatch):
 def test_planner_split_counts(m, n, k, splits):
     assert L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k) == splits * m * n * 4
     assert L.orca_op_linear_workspace_bytes(L.ORCA_F32, m, n, k) == 0
+
+
+# the split tail of the four-wave launches, seen through its workspace
+# (fp32 partial tiles, tail tiles x splits x 256 x 256 or 256 x 192): only
+# when the last round of 256 workgroups is at most half full
+@pytest.mark.parametrize("m,n,k,tail_tiles,splits,bn", [
+    (3698, 36864, 12288, 112, 2, 256),    # 175B layer QKV: 2,160 tiles = 8 rounds + 112
+    (3698, 49152, 12288, 64, 4, 256),     # FFN1: 2,880 = 11 rounds + 64
+    (3698, 12288, 12288, 0, 0, 256),      # output projection: 720 = 2 rounds + 208
+    (3698, 12288, 49152, 0, 0, 256),      # FFN2: the same tiles
+    (2176, 15360, 5120, 0, 0, 192),       # 13B: 720 tiles, 2 rounds + 208
+    (1100, 15360, 4096, 44, 4, 256),      # the GPU test's shapes
+])
+def test_planner_split_tail(m, n, k, tail_tiles, splits, bn, monkeypatch):
+    monkeypatch.delenv("ORCA_GEMM_TAIL", raising=False)
+    if (m, n, k) == (1100, 15360, 4096):
+        monkeypatch.setenv("ORCA_GEMM_VARIANT", "12")
+    else:
+        monkeypatch.delenv("ORCA_GEMM_VARIANT", raising=False)
+    assert L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k) == \
+        tail_tiles * splits * 256 * bn * 4
+    monkeypatch.setenv("ORCA_GEMM_TAIL", "0")
+    assert L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k) == 0

@@ -263,3 +263,76 @@ def test_split_attention(dtype, hidden, heads, shape):
 def dm_for(work, fill=True, **kw):
     from orca_selective_iteration_amd.runner import DeviceModel
     return DeviceModel(work, device=DEV, fill_caches=fill, **kw)
+
+
+# hybrid launches of the four-wave tiles: the last, at most half-full round
+# of tiles split over K (fp32 partials added by the tail reduce with the
+# epilogue).  (1100, 15360, 4096) on 256 x 256 tiles: 5 x 60 = 300 tiles =
+# one round + 44 tail tiles in 4 splits; (1100, 14400, 4096) on 256 x 192:
+# 5 x 75 = 375 tiles = one round + 119 in 2 splits.  The whole output is
+# compared with the same launch without the tail (ORCA_GEMM_TAIL=0: only the
+# summation order differs), and sampled rows, among them the ragged last row
+# tile, with the oracle.
+@pytest.mark.parametrize("variant,n", [("12", 15360), ("13", 14400)])
+@pytest.mark.parametrize("epi", [L.ORCA_EPI_BIAS, L.ORCA_EPI_BIAS_GELU, L.ORCA_EPI_BIAS_RESID])
+def test_hybrid_split_tail(variant, n, epi, monkeypatch):
+    m, k = 1100, 4096
+    print(f"case hybrid tail variant {variant} m={m} n={n} k={k} epi={epi}", flush=True)
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", variant)
+    rng = np.random.default_rng(n + epi)
+    a = draw(rng, (m, k), 1.0, "bf16")
+    w = draw(rng, (n, k), 0.02 * 32 / np.sqrt(k), "bf16")
+    b = draw(rng, n, 0.02, "bf16")
+    init = rng.standard_normal((m, n)).astype(np.float32) if epi == L.ORCA_EPI_BIAS_RESID else None
+    nb = L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k)
+    assert nb > 0, "expected a split tail"
+    ad, wd, bd = dev(a, "bf16"), dev(w, "bf16"), dev(b, "bf16")
+    outs = []
+    for tail in ("1", "0"):
+        monkeypatch.setenv("ORCA_GEMM_TAIL", tail)
+        out = (torch.from_numpy(init).to(DEV) if init is not None
+               else torch.empty((m, n), dtype=torch.bfloat16, device=DEV))
+        ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device=DEV)
+        L.orca_op_linear(L.ORCA_BF16, epi, ad, wd, bd, out, m, n, k, ws, nb)
+        outs.append(host(out))
+    assert np.isfinite(outs[0]).all()
+    assert rel_err(outs[0], outs[1]) < 1e-2
+    rows = np.concatenate([np.arange(0, 8), np.arange(500, 508), np.arange(m - 40, m)])
+    ref = om.linear(a[rows].astype(np.float64), w.astype(np.float64), b.astype(np.float64))
+    if epi == L.ORCA_EPI_BIAS_GELU:
+        ref = om.gelu_tanh(ref)
+    if init is not None:
+        ref = init[rows].astype(np.float64) + ref
+    assert rel_err(outs[0][rows], ref) < TOL["bf16"]
+
+
+def test_hybrid_split_tail_qkv(monkeypatch):
+    """The QKV projection's split tail: the same Q rows and pool slots as the
+    launch without it, and the oracle's on sampled rows."""
+    m, hidden, heads = 1100, 5120, 40       # 256 x 256 tiles: 300 = 256 + 44
+    d, cap = hidden // heads, 1500
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", "12")
+    nb = L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, 3 * hidden, hidden)
+    assert nb > 0
+    rng = np.random.default_rng(5)
+    a = draw(rng, (m, hidden), 1.0, "bf16")
+    w = draw(rng, (3 * hidden, hidden), 0.02, "bf16")
+    b = draw(rng, 3 * hidden, 0.02, "bf16")
+    dst = rng.permutation(cap)[:m].astype(np.int32)
+    res = []
+    for tail in ("1", "0"):
+        monkeypatch.setenv("ORCA_GEMM_TAIL", tail)
+        kp = torch.zeros((heads, cap, d), dtype=torch.bfloat16, device=DEV)
+        vp = torch.zeros((heads, cap, d), dtype=torch.bfloat16, device=DEV)
+        q = torch.empty((m, hidden), dtype=torch.bfloat16, device=DEV)
+        ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device=DEV)
+        L.orca_op_qkv(L.ORCA_BF16, dev(a, "bf16"), dev(w, "bf16"), dev(b, "bf16"), q, kp, vp,
+                      torch.from_numpy(dst).to(DEV), m, hidden, heads, cap, ws, nb)
+        res.append((host(q), host(kp), host(vp)))
+    for x, y in zip(res[0], res[1]):
+        assert rel_err(x, y) < 1e-2
+    rows = np.concatenate([np.arange(0, 4), np.arange(m - 20, m)])
+    ref = om.linear(a[rows].astype(np.float64), w.astype(np.float64), b.astype(np.float64))
+    assert rel_err(res[0][0][rows], ref[:, :hidden]) < TOL["bf16"]
+    kref = ref[:, hidden:2 * hidden].reshape(len(rows), heads, d).transpose(1, 0, 2)
+    assert rel_err(res[0][1][:, dst[rows]], kref) < TOL["bf16"]
