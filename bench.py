@@ -126,9 +126,12 @@ def measured_mfma_util(workload):
     return {k: v for k, v in vals.items()} or None
 
 
-# kernels each timed region launches, as rocprofv3 names them
-TRAFFIC_KERNELS = {"iteration": ("gemm_bf16", "gemm_w4", "gemm_d4", "gemm_ws", "skinny_reduce"),
-                   "decode": ("attn_split", "attn_combine"), "copy": ("copyBuffer",)}
+# kernels each timed region launches, as rocprofv3 names them (from_f32 runs
+# once per iteration: it counts the iterations of a profiled run)
+TRAFFIC_KERNELS = {"iteration": ("gemm_bf16", "gemm_w4", "gemm_d4", "gemm_ws", "skinny_reduce",
+                                 "tail_reduce"),
+                   "decode": ("attn_split", "attn_combine"), "copy": ("copyBuffer",),
+                   "marker": ("from_f32",)}
 
 
 def _counter_sums(path, prefixes):
@@ -162,18 +165,31 @@ def summarize_traffic(src, workload):
     copy_w = max(s / n for s, n in cw.values())
     fs, ws = gib_kib / copy_f, gib_kib / copy_w
     out = {"workload": workload, "fetch_scale": fs, "write_scale": ws}
+    from orca_selective_iteration_amd import synth
+    layers = synth.workload(workload).layers
     for key, what, files in (("gemm", "iteration", GEMM_FILES), ("decode", "decode", ATTN_FILES)):
         f, w = run(what, "FETCH_SIZE"), run(what, "WRITE_SIZE")
         if not f:
             continue
-        launches = sum(n for _, n in f.values())
+        if key == "gemm":
+            # per Linear step (QKV, output projection, FFN1 or FFN2 of one
+            # layer, with the split kernels and reduces it launches): every
+            # GEMM dispatch of the run over 4 x layers x iterations
+            iters = sum(n for _, n in _counter_sums(
+                os.path.join(src, f"pmc_{what}_FETCH_SIZE", "run_counter_collection.csv"),
+                TRAFFIC_KERNELS["marker"]).values())
+            units = 4 * layers * max(iters, 1)
+            unit = "Linear step"
+        else:
+            # per decode-attention call: one attn_split launch each
+            units = sum(n for k, (_, n) in f.items() if "attn_split" in k)
+            unit = "call"
         out[key] = {"kernels": sorted(f), "source_hash": source_hash(files),
-                    "launches": launches,
-                    "fetch_kib_per_launch": {k: round(s / n, 1) for k, (s, n) in f.items()},
-                    "write_kib_per_launch": {k: round(s / n, 1) for k, (s, n) in w.items()},
-                    # per launch, averaged over every launch of the region
-                    "fetch_bytes": sum(s for s, _ in f.values()) * 1024 * fs / launches,
-                    "write_bytes": sum(s for s, _ in w.values()) * 1024 * ws / launches}
+                    "unit": unit, "units": units,
+                    "fetch_kib_per_dispatch": {k: round(s / n, 1) for k, (s, n) in f.items()},
+                    "write_kib_per_dispatch": {k: round(s / n, 1) for k, (s, n) in w.items()},
+                    "fetch_bytes": sum(s for s, _ in f.values()) * 1024 * fs / units,
+                    "write_bytes": sum(s for s, _ in w.values()) * 1024 * ws / units}
     util = {}
     path = os.path.join(src, "pmc_iteration_MfmaUtil", "run_counter_collection.csv")
     if os.path.exists(path):
@@ -280,11 +296,13 @@ def gemm_roofline(L, model, work, reps, log):
     common = {"kernel": ("the flattened Linear launches (QKV, output projection, FFN1, FFN2) of "
                          "every layer, timed inside the iteration"),
               "launches_per_iteration": 4 * work.layers,
+              "launch_unit": ("one Linear step of one layer (QKV, output projection, FFN1 or "
+                              "FFN2, with the split-K kernels and reduces it launches)"),
               "algorithmic_flops_per_launch": int(flops / 4),
               "algorithmic_bytes_per_launch": int(nbytes / 4),
               "ms_per_launch": round(ms / 4, 4),
               "traffic": tr["bytes"] if tr else None,
-              "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
+              "traffic_unit": "bytes per Linear step (HBM read + write, rocprofv3 counters)",
               "mfma_util_percent_counter": measured_mfma_util(work.name),
               "per_step": per}
     if flops / nbytes >= ridge:
