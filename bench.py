@@ -150,6 +150,56 @@ def _counter_sums(path, prefixes):
     return vals
 
 
+XCDS, SIMDS = 8, 1024
+MFMA_FLOP_PER_SIMD_CLOCK = 1024   # v_mfma_f32_32x32x16_bf16: 32*32*16*2 FLOP in 32 cycles
+
+
+def clock_counters(path):
+    """Shader clock and MFMA busy fraction of each GEMM kernel from one
+    rocprofv3 pass of GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES: rocprofv3
+    sums GRBM_GUI_ACTIVE over the XCDs, so the clock is that sum / XCDs / the
+    dispatch's duration.  Kernels averaging under 0.2 ms are left out (the
+    counter window outlasts the dispatch by a few microseconds)."""
+    import csv
+    if not os.path.exists(path):
+        return {}
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if not any(p in name for p in TRAFFIC_KERNELS["iteration"]):
+                continue
+            d = per.setdefault((r["Dispatch_Id"], name.split("(")[0].replace("void ", "")), {})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            d["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    agg = {}
+    for (_, k), v in per.items():
+        a = agg.setdefault(k, [0.0, 0.0, 0.0, 0])
+        a[0] += v.get("GRBM_GUI_ACTIVE", 0.0)
+        a[1] += v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        a[2] += v["dur"]
+        a[3] += 1
+    out = {}
+    for k, (gui, mfma, dur, n) in agg.items():
+        if n == 0 or dur / n < 2e-4 or gui <= 0:
+            continue
+        ghz = gui / XCDS / dur / 1e9
+        out[k] = {"clock_ghz": round(ghz, 3),
+                  "mfma_busy_percent": round(100 * mfma / (gui / XCDS * SIMDS), 1),
+                  "mfma_ceiling_tflops_at_clock":
+                      round(ghz * 1e9 * SIMDS * MFMA_FLOP_PER_SIMD_CLOCK / 1e12, 1)}
+    return out
+
+
+def measured_clock(workload):
+    """The committed clock pass of the GEMM kernels; None when absent or
+    stale."""
+    rec = committed_counters(workload).get("clock")
+    if not rec or rec.get("source_hash") != source_hash(GEMM_FILES):
+        return None
+    return rec.get("iteration") or None
+
+
 def summarize_traffic(src, workload):
     """HBM bytes per launch of the iteration's GEMM launches and of the
     decode attention from the counter runs, each counter scaled by what it
@@ -197,6 +247,9 @@ def summarize_traffic(src, workload):
                 _counter_sums(path, TRAFFIC_KERNELS["iteration"]).items()}
     if util:
         out["mfma_util_percent"] = {"source_hash": source_hash(GEMM_FILES), "iteration": util}
+    clock = clock_counters(os.path.join(src, "pmc_iteration_clock", "run_counter_collection.csv"))
+    if clock:
+        out["clock"] = {"source_hash": source_hash(GEMM_FILES), "iteration": clock}
     dst = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
     with open(dst, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -304,6 +357,7 @@ def gemm_roofline(L, model, work, reps, log):
               "traffic": tr["bytes"] if tr else None,
               "traffic_unit": "bytes per Linear step (HBM read + write, rocprofv3 counters)",
               "mfma_util_percent_counter": measured_mfma_util(work.name),
+              "clock_counter": measured_clock(work.name),
               "per_step": per}
     if flops / nbytes >= ridge:
         return {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
