@@ -685,9 +685,20 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
   // offsets from a uniform base keep each address to one register
   const int ch = tid & 7;
   uint32_t offA[LA], offB[LB];
+  // A rows past M (in the last row tile) read zeros: their offset is the
+  // resource's size, and a buffer read at or past num_records returns 0.
+  // The clock is power-limited, and MFMAs on zero operands draw less than
+  // on copies of a real row (the 13B iteration -1.0%, the 175B-layer one
+  // -0.6%).  Near 4 GB of A, where the size plus a K step's offset could
+  // wrap 32 bits, the rows are clamped to M - 1 instead.
+  const size_t a_bytes = ((size_t)M * K - (size_t)k0 * BK) * 2;
+  const bool zero_rows = a_bytes + (size_t)K * 2 < 0xffffffffu;
 #pragma unroll
-  for (int i = 0; i < LA; ++i)
-    offA[i] = (uint32_t)(min(tm * BM + (tid >> 3) + 32 * i, M - 1) * K + ch * 8) * 2u;
+  for (int i = 0; i < LA; ++i) {
+    const int row = tm * BM + (tid >> 3) + 32 * i;
+    offA[i] = row < M ? (uint32_t)(row * K + ch * 8) * 2u
+                      : zero_rows ? (uint32_t)a_bytes : (uint32_t)((M - 1) * K + ch * 8) * 2u;
+  }
 #pragma unroll
   for (int i = 0; i < LB; ++i)
     offB[i] = (uint32_t)(min(tn * BN + (tid >> 3) + 32 * i, N - 1) * K + ch * 8) * 2u;
@@ -698,8 +709,8 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
   // buffer loads: a 32-bit lane offset plus the K step's offset in a scalar
   // register, so no 64-bit address is formed per load.  The resource's last
   // word (0x00020000) selects raw 32-bit data, as gfx9-family raw buffer
-  // loads expect; num_records is the operand's size (the clamped offsets
-  // never reach past it, and a read past it would return zeros)
+  // loads expect; num_records is the operand's size (valid rows never reach
+  // past it; A's padding rows start at it and read zeros)
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
       (void*)A, (short)0,
       (int)(uint32_t)std::min<size_t>(((size_t)M * K - (size_t)k0 * BK) * 2, 0xffffffffu),
