@@ -105,7 +105,7 @@ typedef struct {
   int32_t ffn;          /* F */
   int32_t dtype;        /* orca_dtype */
   float   ln_eps;       /* LayerNorm epsilon (inside the square root) */
-  int64_t kv_capacity;  /* token slots per layer and head in each pool */
+  int64_t kv_capacity;  /* token slots per layer and head in the K/V pool */
 } orca_model_desc;
 
 /* One layer's parameters, device pointers of the model dtype.  The block is
@@ -154,10 +154,12 @@ typedef struct orca_ctx orca_ctx;
  *   desc        model shape (copied)
  *   layers      host array [desc->layers] of device weight pointers (copied;
  *               the weights themselves are borrowed)
- *   k_pool,
- *   v_pool      device [layers][heads][kv_capacity][d] of the model dtype
- *               (borrowed); entry t of head h of a request at layer l is
- *               pool[l][h][kv_base + t][0..d-1]
+ *   kv_pool     device [layers][heads][kv_capacity][2][d] of the model dtype
+ *               (borrowed): entry t of head h of a request at layer l has
+ *               its key at kv_pool[l][h][kv_base + t][0][0..d-1] and its
+ *               value right after it, at [1][0..d-1].  A slot's key and
+ *               value rows are adjacent, so the attention over a request's
+ *               cache reads one contiguous stream per head, not two
  *   kv          optional (may be NULL) allocator whose capacity equals
  *               desc->kv_capacity; when given, every request's range
  *               kv_base .. kv_base+kv_len+q_len-1 must lie inside one of its
@@ -167,7 +169,7 @@ typedef struct orca_ctx orca_ctx;
  *               they size the workspace and the pinned metadata buffers
  * Allocates pinned host staging memory (hipHostMalloc); no device memory. */
 orca_status orca_create(const orca_model_desc* desc, const orca_layer_weights* layers,
-                        void* k_pool, void* v_pool, const orca_kv* kv,
+                        void* kv_pool, const orca_kv* kv,
                         int32_t max_rows, int32_t max_reqs, orca_ctx** out);
 orca_status orca_destroy(orca_ctx* ctx);
 
@@ -294,14 +296,15 @@ orca_status orca_op_linear_noalloc(int32_t dtype, int32_t epilogue, const void* 
 
 /* The fused QKV projection with the K/V manager's append: for every row m,
  * [q|k|v] = a[m] W_qkv^T + b_qkv; q goes to q_out[m][0..H-1]; k and v of
- * head h go to k_pool_l[h][row_dst[m]][..] and v_pool_l[h][row_dst[m]][..].
- * row_dst: device int32 [m], each in [0, kv_capacity).  k_pool_l/v_pool_l
- * point at one layer's pool [heads][kv_capacity][d].  workspace / ws_bytes
+ * head h go to kv_pool_l[h][row_dst[m]][0][..] and kv_pool_l[h][row_dst[m]][1][..].
+ * row_dst: device int32 [m], each in [0, kv_capacity).  kv_pool_l points at
+ * one layer's pool [heads][kv_capacity][2][d] (the layout of orca_create's
+ * kv_pool).  workspace / ws_bytes
  * as for orca_op_linear with n = 3 * hidden, k = hidden.  ([houmin] 3.1.2: the
  * QKV Linear yields 3H columns; the split before attention is index
  * arithmetic; the new K/V of every token is appended to its request.) */
 orca_status orca_op_qkv(int32_t dtype, const void* a, const void* w_qkv, const void* b_qkv,
-                        void* q_out, void* k_pool_l, void* v_pool_l, const int32_t* row_dst,
+                        void* q_out, void* kv_pool_l, const int32_t* row_dst,
                         int32_t m, int32_t hidden, int32_t heads, int64_t kv_capacity,
                         void* workspace, size_t ws_bytes, void* stream);
 

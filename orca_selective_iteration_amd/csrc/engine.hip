@@ -43,8 +43,7 @@ bool head_dim_ok(int dtype, int d) {
 struct orca_ctx {
   orca_model_desc desc{};
   std::vector<orca_layer_weights> layers;
-  void* k_pool = nullptr;
-  void* v_pool = nullptr;
+  void* kv_pool = nullptr;   // [layers][heads][cap][2][d]
   const orca_kv* kv = nullptr;
   int32_t max_rows = 0, max_reqs = 0;
   int64_t max_items = 0, max_pf = 0;
@@ -64,8 +63,9 @@ struct orca_ctx {
   bool probe_recorded = false;
   std::vector<hipEvent_t> probe_ev;
 
+  // one layer of the pool: [heads][cap][2][d]
   size_t layer_pool_elems() const {
-    return (size_t)desc.heads * (size_t)desc.kv_capacity * (size_t)(desc.hidden / desc.heads);
+    return (size_t)desc.heads * (size_t)desc.kv_capacity * 2 * (size_t)(desc.hidden / desc.heads);
   }
 };
 
@@ -248,9 +248,9 @@ orca_status stage(orca_ctx* c, const orca_req_desc* reqs, int32_t n, char* ws, h
 extern "C" {
 
 orca_status orca_create(const orca_model_desc* desc, const orca_layer_weights* layers,
-                        void* k_pool, void* v_pool, const orca_kv* kv, int32_t max_rows,
+                        void* kv_pool, const orca_kv* kv, int32_t max_rows,
                         int32_t max_reqs, orca_ctx** out) {
-  ORCA_CHECK_ARG(desc && layers && k_pool && v_pool && out, "orca_create: NULL argument");
+  ORCA_CHECK_ARG(desc && layers && kv_pool && out, "orca_create: NULL argument");
   const orca_model_desc& d = *desc;
   ORCA_CHECK_ARG(d.dtype == ORCA_F32 || d.dtype == ORCA_BF16, "unknown dtype %d", d.dtype);
   ORCA_CHECK_ARG(d.layers >= 1 && d.hidden >= 64 && d.heads >= 1 && d.ffn >= 64,
@@ -278,8 +278,7 @@ orca_status orca_create(const orca_model_desc* desc, const orca_layer_weights* l
   ORCA_CHECK_ARG(c != nullptr, "out of host memory");
   c->desc = d;
   c->layers.assign(layers, layers + d.layers);
-  c->k_pool = k_pool;
-  c->v_pool = v_pool;
+  c->kv_pool = kv_pool;
   c->kv = kv;
   c->max_rows = max_rows;
   c->max_reqs = max_reqs;
@@ -366,8 +365,7 @@ static orca_status run_attention(orca_ctx* c, int layer, AttnArgs aa, const void
   const size_t pool = c->layer_pool_elems() * dsize(c->desc.dtype);
   aa.q = q;
   aa.o = o;
-  aa.k_pool = static_cast<char*>(c->k_pool) + pool * layer;
-  aa.v_pool = static_cast<char*>(c->v_pool) + pool * layer;
+  aa.kv_pool = static_cast<char*>(c->kv_pool) + pool * layer;
   HIP_TRY(launch_attention(aa, s), "attention launch");
   return ORCA_OK;
 }
@@ -413,8 +411,8 @@ orca_status orca_iteration(orca_ctx* c, const orca_req_desc* reqs, int32_t n_req
           "LN1");
   for (int l = 0; l < d.layers; ++l) {
     const orca_layer_weights& w = c->layers[l];
-    QkvDest qd{q, static_cast<char*>(c->k_pool) + pool * l, static_cast<char*>(c->v_pool) + pool * l,
-               row_dst, H, H / d.heads, d.kv_capacity};
+    QkvDest qd{q, static_cast<char*>(c->kv_pool) + pool * l, row_dst, H, H / d.heads,
+               d.kv_capacity};
     HIP_TRY(mark(l, ORCA_STEP_QKV, 0), "timing event");
     HIP_TRY(launch_linear(dt, EPI_QKV, a, w.w_qkv, w.b_qkv, nullptr, &qd, R, 3 * H, H, gp, gpb, s), "QKV");
     HIP_TRY(mark(l, ORCA_STEP_QKV, 1), "timing event");
@@ -528,7 +526,7 @@ orca_status orca_op_linear(int32_t dtype, int32_t epilogue, const void* a, const
 }
 
 orca_status orca_op_qkv(int32_t dtype, const void* a, const void* w_qkv, const void* b_qkv,
-                        void* q_out, void* k_pool_l, void* v_pool_l, const int32_t* row_dst,
+                        void* q_out, void* kv_pool_l, const int32_t* row_dst,
                         int32_t m, int32_t hidden, int32_t heads, int64_t kv_capacity,
                         void* workspace, size_t ws_bytes, void* stream) {
   clear_error();
@@ -540,9 +538,9 @@ orca_status orca_op_qkv(int32_t dtype, const void* a, const void* w_qkv, const v
     set_error("unsupported shape: hidden %d head_dim %d", hidden, hidden / heads);
     return ORCA_ERR_UNSUPPORTED;
   }
-  ORCA_CHECK_ARG(m == 0 || (a && w_qkv && b_qkv && q_out && k_pool_l && v_pool_l && row_dst),
+  ORCA_CHECK_ARG(m == 0 || (a && w_qkv && b_qkv && q_out && kv_pool_l && row_dst),
                  "NULL argument");
-  QkvDest qd{q_out, k_pool_l, v_pool_l, row_dst, hidden, hidden / heads, kv_capacity};
+  QkvDest qd{q_out, kv_pool_l, row_dst, hidden, hidden / heads, kv_capacity};
   HIP_TRY(launch_linear(dtype, EPI_QKV, a, w_qkv, b_qkv, nullptr, &qd, m, 3 * hidden, hidden,
                         workspace, ws_bytes,
                         static_cast<hipStream_t>(stream)), "qkv launch");

@@ -60,7 +60,8 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 
 // One output column of a Linear layer, fixed per lane before the epilogue:
 // where element (m, n) goes is col.ptr + m * col.stride, or for the K/V
-// blocks of the QKV projection col.ptr + row_dst[m] * d (the pool slot).
+// blocks of the QKV projection col.ptr + row_dst[m] * 2d (the pool slot,
+// whose key row is followed by its value row).
 template <typename T, int EPI>
 struct EpiCol {
   T* ptr;
@@ -75,14 +76,14 @@ struct EpiCol {
         stride = H;
       } else {
         int c = n - H;
-        T* pool = (T*)ep.qkv.k_pool;
+        T* pool = (T*)ep.qkv.kv_pool;
         if (c >= H) {
           c -= H;
-          pool = (T*)ep.qkv.v_pool;
+          pool += d;   // the value row follows the key row
         }
         const int h = c / d, dd = c - h * d;
-        ptr = pool + (size_t)h * ep.qkv.cap * d + dd;
-        stride = d;
+        ptr = pool + (size_t)h * ep.qkv.cap * 2 * d + dd;
+        stride = 2 * d;
         slot = true;
       }
     } else {

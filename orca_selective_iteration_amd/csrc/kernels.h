@@ -21,8 +21,7 @@ hipError_t launch_from_f32(int dtype, const float* in, void* out, int64_t n, hip
 // ---- Linear layers (gemm.hip) ---------------------------------------------
 struct QkvDest {
   void* q_out;          // [m][H]
-  void* k_pool;         // one layer: [heads][cap][d]
-  void* v_pool;
+  void* kv_pool;        // one layer: [heads][cap][2][d] (key row, then value row)
   const int32_t* row_dst;
   int hidden, head_dim;
   int64_t cap;
@@ -81,8 +80,7 @@ struct AttnArgs {
   int64_t cap;
   const void* q;          // [rows][H]
   void* o;                // [rows][H]
-  const void* k_pool;     // one layer: [heads][cap][d]
-  const void* v_pool;
+  const void* kv_pool;    // one layer: [heads][cap][2][d] (key row, then value row)
   const DevReq* reqs;
   const SplitItem* items;  int n_items;
   const SplitRow* srows;   int n_srows;

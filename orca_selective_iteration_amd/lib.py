@@ -74,7 +74,7 @@ def _declare(lib):
         "orca_kv_used": (I64, [V]),
         "orca_kv_capacity": (I64, [V]),
         "orca_kv_reservation": (I64, [V, I64]),
-        "orca_create": (c_int32, [POINTER(orca_model_desc), POINTER(orca_layer_weights), V, V, V,
+        "orca_create": (c_int32, [POINTER(orca_model_desc), POINTER(orca_layer_weights), V, V,
                                   I32, I32, POINTER(V)]),
         "orca_destroy": (c_int32, [V]),
         "orca_workspace_bytes": (S, [V]),
@@ -86,7 +86,7 @@ def _declare(lib):
         "orca_op_linear_variant": (I32, [I32, I32, I32, I32]),
         "orca_op_linear": (c_int32, [I32, I32, V, V, V, V, I32, I32, I32, V, S, V]),
         "orca_op_linear_noalloc": (c_int32, [I32, I32, V, V, V, V, I32, I32, I32, V]),
-        "orca_op_qkv": (c_int32, [I32, V, V, V, V, V, V, V, I32, I32, I32, I64, V, S, V]),
+        "orca_op_qkv": (c_int32, [I32, V, V, V, V, V, V, I32, I32, I32, I64, V, S, V]),
         "orca_op_attention": (c_int32, [V, I32, POINTER(orca_req_desc), I32, V, V, V, S, V]),
         "orca_sched_create": (c_int32, [V, I32, I32, I32, POINTER(V)]),
         "orca_sched_destroy": (None, [V]),
@@ -223,16 +223,18 @@ def orca_kv_reservation(kv: int, base: int) -> int:
 # ------------------------------------------------------------------ engine
 
 def orca_create(layers: int, hidden: int, heads: int, ffn: int, dtype: int, ln_eps: float,
-                kv_capacity: int, weights: Sequence[dict], k_pool, v_pool, kv: Optional[int],
+                kv_capacity: int, weights: Sequence[dict], kv_pool, kv: Optional[int],
                 max_rows: int, max_reqs: int) -> int:
-    """weights: one dict per layer mapping LAYER_KEYS to tensors / addresses."""
+    """weights: one dict per layer mapping LAYER_KEYS to tensors / addresses;
+    kv_pool: [layers][heads][kv_capacity][2][d] (each slot's key row, then its
+    value row)."""
     desc = orca_model_desc(layers, hidden, heads, ffn, dtype, ln_eps, kv_capacity)
     arr = (orca_layer_weights * layers)()
     for l, w in enumerate(weights):
         arr[l] = orca_layer_weights(*[ptr(w[k]) for k in LAYER_KEYS])
     h = c_void_p()
-    _check(load().orca_create(byref(desc), arr, ptr(k_pool), ptr(v_pool), kv, max_rows,
-                              max_reqs, byref(h)), "orca_create")
+    _check(load().orca_create(byref(desc), arr, ptr(kv_pool), kv, max_rows, max_reqs,
+                              byref(h)), "orca_create")
     return h.value
 
 
@@ -292,11 +294,12 @@ def orca_op_linear_noalloc(dtype: int, epilogue: int, a, w, bias, out, m: int, n
            "orca_op_linear_noalloc")
 
 
-def orca_op_qkv(dtype: int, a, w_qkv, b_qkv, q_out, k_pool_l, v_pool_l, row_dst, m: int,
+def orca_op_qkv(dtype: int, a, w_qkv, b_qkv, q_out, kv_pool_l, row_dst, m: int,
                 hidden: int, heads: int, kv_capacity: int, workspace=None, ws_bytes: int = 0,
                 stream=None) -> None:
-    _check(load().orca_op_qkv(dtype, ptr(a), ptr(w_qkv), ptr(b_qkv), ptr(q_out), ptr(k_pool_l),
-                              ptr(v_pool_l), ptr(row_dst), m, hidden, heads, kv_capacity,
+    """kv_pool_l: one layer's pool [heads][kv_capacity][2][d]."""
+    _check(load().orca_op_qkv(dtype, ptr(a), ptr(w_qkv), ptr(b_qkv), ptr(q_out), ptr(kv_pool_l),
+                              ptr(row_dst), m, hidden, heads, kv_capacity,
                               ptr(workspace), ws_bytes, stream_handle(stream)), "orca_op_qkv")
 
 

@@ -54,10 +54,12 @@ class DeviceModel:
                                                          self.tdt))
                 if l % 10 == 9:
                     log(f"weights: {l + 1}/{work.layers} layers drawn")
-        # pools [layers][heads][cap][d]
-        shape = (work.layers, work.heads, self.cap, d)
-        self.k_pool = torch.empty(shape, dtype=self.tdt, device=device)
-        self.v_pool = torch.empty(shape, dtype=self.tdt, device=device)
+        # one pool [layers][heads][cap][2][d]: each slot's key row, then its
+        # value row; k_pool and v_pool are the two [layers][heads][cap][d] views
+        self.kv_pool = torch.empty((work.layers, work.heads, self.cap, 2, d), dtype=self.tdt,
+                                   device=device)
+        self.k_pool = self.kv_pool[:, :, :, 0]
+        self.v_pool = self.kv_pool[:, :, :, 1]
         # reservations, in batch order
         self.kv = L.orca_kv_create(self.cap) if use_kv_manager else None
         self.bases: List[int] = []
@@ -72,13 +74,13 @@ class DeviceModel:
             if host is not None:
                 self.load_host_caches(host.caches)
             else:
-                log(f"filling K/V pools: 2 x {self.k_pool.numel() * self.k_pool.element_size() / 1e9:.1f} GB")
+                log(f"filling the K/V pool: {self.kv_pool.numel() * self.kv_pool.element_size() / 1e9:.1f} GB")
                 self.fill_device_caches(seed)
                 log("K/V pools filled")
         self.max_rows = int(max_rows or max(work.rows, 1))
         self.max_reqs = int(max_reqs or max(work.n_reqs, 1))
         self.ctx = L.orca_create(work.layers, work.hidden, work.heads, work.ffn, self.odt,
-                                 work.eps, self.cap, self.weights, self.k_pool, self.v_pool,
+                                 work.eps, self.cap, self.weights, self.kv_pool,
                                  self.kv, self.max_rows, self.max_reqs)
         self.ws_bytes = L.orca_workspace_bytes(self.ctx)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
@@ -100,9 +102,9 @@ class DeviceModel:
                 self.v_pool[l, :, b:b + kv] = vt.permute(1, 0, 2)
 
     def fill_device_caches(self, seed: int):
-        """Seeded N(0,1) in every slot of both pools (cached and free slots)."""
-        device_normal_(self.k_pool, seed * 7919 + 1)
-        device_normal_(self.v_pool, seed * 7919 + 2)
+        """Seeded N(0,1) in every key and value row of the pool (cached and
+        free slots)."""
+        device_normal_(self.kv_pool, seed * 7919 + 1)
 
     def cache_rows(self, layer: int, req: int, lo: int, hi: int):
         """K, V entries lo..hi-1 of request `req` at `layer` as [n, H] fp32 host arrays."""

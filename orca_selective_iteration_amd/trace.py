@@ -60,12 +60,12 @@ class TraceEngine:
             kv_slots = int((free * hbm_fraction - ws_guess) // per_token)
         self.cap = int(kv_slots)
         log(f"K/V pool: {self.cap} token slots ({self.cap * per_token / 1e9:.1f} GB)")
-        shape = (work.layers, work.heads, self.cap, work.head_dim)
-        self.k_pool = torch.empty(shape, dtype=self.tdt, device="cuda")
-        self.v_pool = torch.empty(shape, dtype=self.tdt, device="cuda")
+        # [layers][heads][cap][2][d]: each slot's key row, then its value row
+        self.kv_pool = torch.empty((work.layers, work.heads, self.cap, 2, work.head_dim),
+                                   dtype=self.tdt, device="cuda")
         self.kv = L.orca_kv_create(self.cap)
         self.ctx = L.orca_create(work.layers, work.hidden, work.heads, work.ffn, self.odt,
-                                 work.eps, self.cap, self.weights, self.k_pool, self.v_pool,
+                                 work.eps, self.cap, self.weights, self.kv_pool,
                                  self.kv, self.max_rows, self.max_reqs)
         self.ws_bytes = L.orca_workspace_bytes(self.ctx)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
@@ -213,7 +213,7 @@ class TraceEngine:
             L.orca_kv_destroy(self.kv)
             self.kv = None
         self.weights = []
-        self.k_pool = self.v_pool = self.ws = self.x = self.y = None
+        self.kv_pool = self.ws = self.x = self.y = None
         try:
             import torch
             torch.cuda.empty_cache()

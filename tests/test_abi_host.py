@@ -241,15 +241,15 @@ def test_scheduler_argument_errors():
 def test_engine_validation_fails_before_gpu():
     w = {k: 16 for k in L.LAYER_KEYS}                      # fake addresses: never read
     with pytest.raises(L.OrcaError) as e:
-        L.orca_create(1, 64, 4, 256, L.ORCA_F32, 1e-5, 0, [w], 16, 16, None, 8, 4)
+        L.orca_create(1, 64, 4, 256, L.ORCA_F32, 1e-5, 0, [w], 16, None, 8, 4)
     assert e.value.status == L.ORCA_ERR_INVALID
     with pytest.raises(L.OrcaError) as e:                  # d = 32 not supported in bf16
-        L.orca_create(1, 128, 4, 256, L.ORCA_BF16, 1e-5, 64, [w], 16, 16, None, 8, 4)
+        L.orca_create(1, 128, 4, 256, L.ORCA_BF16, 1e-5, 64, [w], 16, None, 8, 4)
     assert e.value.status == L.ORCA_ERR_UNSUPPORTED
     kv = L.orca_kv_create(50)
     try:
         with pytest.raises(L.OrcaError) as e:              # capacity mismatch
-            L.orca_create(1, 64, 4, 256, L.ORCA_F32, 1e-5, 64, [w], 16, 16, kv, 8, 4)
+            L.orca_create(1, 64, 4, 256, L.ORCA_F32, 1e-5, 64, [w], 16, kv, 8, 4)
         assert "capacity" in str(e.value)
     finally:
         L.orca_kv_destroy(kv)
@@ -266,7 +266,7 @@ def test_op_validation_fails_before_gpu():
         L.orca_op_layernorm(L.ORCA_F32, 16, 16, 16, 16, 4, 12292, 1e-5)
     assert e.value.status == L.ORCA_ERR_INVALID
     with pytest.raises(L.OrcaError) as e:
-        L.orca_op_qkv(L.ORCA_BF16, 16, 16, 16, 16, 16, 16, 16, 4, 256, 8, 100)
+        L.orca_op_qkv(L.ORCA_BF16, 16, 16, 16, 16, 16, 16, 4, 256, 8, 100)
     assert e.value.status == L.ORCA_ERR_UNSUPPORTED          # head dim 32 in bf16
 
 

@@ -85,11 +85,11 @@ def run_fullsize(name, n_full_depth, init_rows, layers_checked, seed=0):
             assert e < TOL["bf16"], (i, e)
 
         # ---- single layers over the whole batch
-        size = model.k_pool[0].numel() * model.k_pool.element_size()
+        size = model.kv_pool[0].numel() * model.kv_pool.element_size()
         for l in layers_checked:
             ctx = L.orca_create(1, work.hidden, work.heads, work.ffn, model.odt, work.eps,
-                                model.cap, [model.weights[l]], model.k_pool.data_ptr() + l * size,
-                                model.v_pool.data_ptr() + l * size, model.kv, model.max_rows,
+                                model.cap, [model.weights[l]], model.kv_pool.data_ptr() + l * size,
+                                model.kv, model.max_rows,
                                 model.max_reqs)
             try:
                 ws_bytes = L.orca_workspace_bytes(ctx)

@@ -192,12 +192,15 @@ def test_qkv_split_and_append(dtype, m, hidden, heads, variant, monkeypatch):
     w = draw(rng, (3 * hidden, hidden), 0.02, dtype)
     b = draw(rng, 3 * hidden, 0.02, dtype)
     dst = rng.permutation(cap)[:m].astype(np.int32)
-    kp = torch.full((heads, cap, d), 7.0, dtype=tdt(dtype), device=DEV)
-    vp = torch.full((heads, cap, d), -7.0, dtype=tdt(dtype), device=DEV)
+    # one layer's pool [heads][cap][2][d]: key rows 7, value rows -7
+    kvp = torch.empty((heads, cap, 2, d), dtype=tdt(dtype), device=DEV)
+    kvp[:, :, 0] = 7.0
+    kvp[:, :, 1] = -7.0
+    kp, vp = kvp[:, :, 0], kvp[:, :, 1]
     q = torch.empty((m, hidden), dtype=tdt(dtype), device=DEV)
     nb = L.orca_op_linear_workspace_bytes(odt(dtype), m, 3 * hidden, hidden)
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=DEV)
-    L.orca_op_qkv(odt(dtype), dev(a, dtype), dev(w, dtype), dev(b, dtype), q, kp, vp,
+    L.orca_op_qkv(odt(dtype), dev(a, dtype), dev(w, dtype), dev(b, dtype), q, kvp,
                   torch.from_numpy(dst).to(DEV), m, hidden, heads, cap, ws, nb)
     ref = om.linear(a.astype(np.float64), w.astype(np.float64), b.astype(np.float64))
     assert rel_err(host(q), ref[:, :hidden]) < TOL[dtype]
@@ -322,11 +325,11 @@ def test_hybrid_split_tail_qkv(monkeypatch):
     res = []
     for tail in ("1", "0"):
         monkeypatch.setenv("ORCA_GEMM_TAIL", tail)
-        kp = torch.zeros((heads, cap, d), dtype=torch.bfloat16, device=DEV)
-        vp = torch.zeros((heads, cap, d), dtype=torch.bfloat16, device=DEV)
+        kvp = torch.zeros((heads, cap, 2, d), dtype=torch.bfloat16, device=DEV)
+        kp, vp = kvp[:, :, 0], kvp[:, :, 1]
         q = torch.empty((m, hidden), dtype=torch.bfloat16, device=DEV)
         ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device=DEV)
-        L.orca_op_qkv(L.ORCA_BF16, dev(a, "bf16"), dev(w, "bf16"), dev(b, "bf16"), q, kp, vp,
+        L.orca_op_qkv(L.ORCA_BF16, dev(a, "bf16"), dev(w, "bf16"), dev(b, "bf16"), q, kvp,
                       torch.from_numpy(dst).to(DEV), m, hidden, heads, cap, ws, nb)
         res.append((host(q), host(kp), host(vp)))
     for x, y in zip(res[0], res[1]):
