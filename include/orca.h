@@ -27,7 +27,7 @@
  *   - Handles are not thread-safe: one context per stream / thread.
  *
  * Data types.  ORCA_F32: fp32 everywhere.  ORCA_BF16: bf16 storage for
- * weights, activations and the K/V pools; fp32 accumulation in every
+ * weights, activations and the K/V pool; fp32 accumulation in every
  * contraction, fp32 LayerNorm statistics, fp32 softmax, an fp32 residual
  * stream inside the iteration; values are rounded to nearest-even at each
  * bf16 store.
@@ -93,7 +93,7 @@ int64_t orca_kv_capacity(const orca_kv* kv);
 int64_t orca_kv_reservation(const orca_kv* kv, int64_t base);
 
 /* ------------------------------------------------------------------------
- * Engine: the model, its K/V pools and one iteration.
+ * Engine: the model, its K/V pool and one iteration.
  * ---------------------------------------------------------------------- */
 
 /* Decoder shape.  head dim d = hidden / heads.  Supported: hidden % 64 == 0,
@@ -187,7 +187,7 @@ size_t orca_workspace_bytes(const orca_ctx* ctx);
  *   y             device [sum L][H] model dtype: output rows of the last
  *                 layer (may not alias x or the workspace)
  *   workspace     device, >= orca_workspace_bytes(ctx) bytes
- * Appends the K/V rows of every request to the pools, at every layer.
+ * Appends the K/V rows of every request to the pool, at every layer.
  * Metadata goes to the device with one asynchronous copy from a pinned
  * ring of staging buffers; the call does not wait for the GPU except when
  * the ring slot it needs is still being copied from. */
@@ -313,8 +313,8 @@ orca_status orca_op_qkv(int32_t dtype, const void* a, const void* w_qkv, const v
  * increment: one query over kv_len cached entries plus its own new one);
  * outputs land at the request's own rows of o (the merge is index
  * arithmetic).  q, o device [sum L][H] of the context's dtype; the new K/V
- * rows must already be in the pools (orca_op_qkv).  Uses the context's
- * pools at `layer` and its metadata path; workspace as for orca_iteration. */
+ * rows must already be in the pool (orca_op_qkv).  Uses the context's
+ * pool at `layer` and its metadata path; workspace as for orca_iteration. */
 orca_status orca_op_attention(orca_ctx* ctx, int32_t layer, const orca_req_desc* reqs,
                               int32_t n_reqs, const void* q, void* o, void* workspace,
                               size_t ws_bytes, void* stream);

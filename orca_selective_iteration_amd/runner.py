@@ -1,4 +1,4 @@
-"""Device-side setup around the C ABI: allocates the weights, K/V pools and
+"""Device-side setup around the C ABI: allocates the weights, the K/V pool and
 workspace with PyTorch (device memory only), reserves each request's slots
 through the library's K/V manager and calls orca_iteration.  No arithmetic
 of the method happens here; every step of the iteration runs in liborca.so.
@@ -24,7 +24,7 @@ def orca_dtype(dtype: str) -> int:
 
 
 class DeviceModel:
-    """Weights + pools + engine context for one workload on one GPU.
+    """Weights + K/V pool + engine context for one workload on one GPU.
 
     kv_capacity: token slots per layer/head (default: every request's
     kv_len + q_len plus `slack` slots each).
@@ -76,7 +76,7 @@ class DeviceModel:
             else:
                 log(f"filling the K/V pool: {self.kv_pool.numel() * self.kv_pool.element_size() / 1e9:.1f} GB")
                 self.fill_device_caches(seed)
-                log("K/V pools filled")
+                log("K/V pool filled")
         self.max_rows = int(max_rows or max(work.rows, 1))
         self.max_reqs = int(max_reqs or max(work.n_reqs, 1))
         self.ctx = L.orca_create(work.layers, work.hidden, work.heads, work.ffn, self.odt,

@@ -8,7 +8,7 @@ checked exactly:
     sampled increment requests the oracle (float64) replays every layer on
     that request alone, from the same seeded weights and caches, and the
     output rows and the K/V rows appended at every layer are compared;
-  * one layer: a single-layer engine over layer l of the same pools runs the
+  * one layer: a single-layer engine over layer l of the same pool runs the
     whole batch from seeded input rows; the oracle checks the complete first
     initiation prompt (or its first rows, whose causal attention needs no
     later row) and sampled increment requests.

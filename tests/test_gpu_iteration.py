@@ -2,7 +2,7 @@
 
 The oracle (float64) runs every request of the batch through every layer on
 the same seeded inputs (bf16 inputs rounded to bf16 first).  Compared: the
-output rows y and the K/V rows the iteration appended to the pools at every
+output rows y and the K/V rows the iteration appended to the pool at every
 layer.
 """
 import numpy as np

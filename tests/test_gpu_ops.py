@@ -238,7 +238,7 @@ def test_split_attention(dtype, hidden, heads, shape):
     try:
         d = hidden // heads
         rows = work.rows
-        # synthetic pools: cached entries and this iteration's appended entries
+        # synthetic pool: cached entries and this iteration's appended entries
         kp = draw(rng, model.k_pool.shape, 1.0, dtype)
         vp = draw(rng, model.v_pool.shape, 1.0, dtype)
         model.k_pool.copy_(torch.from_numpy(kp))
