@@ -25,6 +25,7 @@
 // resident on the same XCD.
 //
 // fp32 path: a plain LDS-tiled FMA kernel (64 x 64 tile) for fp32 models.
+#include <limits.h>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -1217,17 +1218,19 @@ static void set_splits(int kt, int splits, SplitPlan& p) {
 }
 static long ceil_div_l(long a, long b) { return (a + b - 1) / b; }
 
-// Few rows (up to SPLIT_MAX_M) whose 32/64/128-row tiles are too few to fill
-// the GPU: split K.  A CU streams about as fast with one of these
-// workgroups as with two, so the time goes as the rounds of NUM_CU
-// workgroups times the K steps of one split; the split count minimises
+// Launches whose 32/64/128-row tiles are too few to fill the GPU (few rows,
+// or at 1,000-2,000 rows a narrow output such as a 1024-wide projection,
+// where 128 x 128 tiles leave most CUs idle): split K.  A CU streams about
+// as fast with one of these workgroups as with two (and at more rows two
+// share its MFMAs), so the time goes as the rounds of NUM_CU workgroups
+// times the K steps of one split; the split count minimises
 // that, ties going to fewer splits (each split writes and re-reads an fp32
 // partial plane), within one round of resident workgroups (two per CU,
 // bounded by LDS).  At 64 rows of the 13B layer this gives 2 splits for
 // QKV, 6 for the output projection and FFN2, 3 for FFN1 (measured: 2 and
 // 6 beat the 4-12 splits that fill 512 slots by 8-15%; 3 beats 2 and 4).
 static bool few_rows_plan(int m, int n, int k, SplitPlan& p) {
-  if (m > env_int("ORCA_SPLIT_MAX_M", SPLIT_MAX_M)) return false;
+  if (m > env_int("ORCA_SPLIT_MAX_M", INT_MAX)) return false;   // a cap for sweeps only
   const int kt = k / BK;
   p.tile = m <= 32 ? 0 : m <= 64 ? 1 : 2;
   const int bm = p.tile == 0 ? 32 : p.tile == 1 ? 64 : 128;

@@ -31,13 +31,14 @@ struct QkvDest {
 constexpr int EPI_QKV = 3;
 // internal: fp32 partial sums of a K split, no bias (the few-rows path)
 constexpr int EPI_PARTIAL = 4;
-// bf16 problems whose tiles are too few to fill the GPU (up to SPLIT_MAX_M
-// rows on 32/64/128-row tiles; 256 x 256 tiles short of one round when
-// splitting K fills whole rounds better) take a split-K path when `ws` holds
+// bf16 problems whose tiles are too few to fill the GPU (on 32/64/128-row
+// tiles at most half a round of resident workgroups, at any row count; 256
+// x 256 tiles short of one round when splitting K fills whole rounds
+// better) take a split-K path when `ws` holds
 // linear_workspace_bytes(dtype, m, n, k) bytes (fp32 partial sums);
 // otherwise, and for every other shape, the tiled kernels run and `ws` is
-// not touched.
-constexpr int SPLIT_MAX_M = 1024;
+// not touched.  The half-round test bounds the partial sums: tiles x splits
+// stays within one round, so splits * m * n <= 512 * 128 * 128 elements.
 constexpr int SPLIT_MAX_SPLITS = 16;
 size_t linear_workspace_bytes(int dtype, int m, int n, int k);
 // The tile variant a bf16 launch of this problem takes (ORCA_GEMM_VARIANT
