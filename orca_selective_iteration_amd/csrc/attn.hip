@@ -200,29 +200,76 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 // Initiation rows of a bf16 model: causal attention of a prompt over itself.
 // A 256-thread workgroup takes one head and PREFILL_ROWS = 128 consecutive
 // query positions of one request (32 per wave) and walks the request's keys
-// 0 .. last query position in steps of 64, staging each K step (row-major)
-// and V step (transposed to [d][key]) in LDS.  Scores are computed
-// transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: a lane then owns
-// one query (its column) and 16 of the 32 keys of each MFMA tile, so the
-// softmax max / sum need one cross-lane step (lane ^ 32).  The probabilities
-// feed O^T = V^T P^T straight from the score registers: the keys of the
-// PV MFMA's k-dimension are taken in the order in which the score tile
-// left them in the lanes, and V^T stores the keys of every 16-key group in
-// that order (keys 4-7 and 8-11 swapped), so a lane's eight keys are one
-// 16-byte LDS read and P never moves between lanes.  Online softmax in base 2 with a running max
-// and sum per query; the output tile is transposed through LDS so the
-// [sum L, H] rows are written with 16-byte stores.
+// 0 .. last query position in steps of 64.  Each step's K and V rows are
+// staged row-major in LDS (16-byte writes, two stages: the next step is
+// written while this one is read).
+//
+// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+// a lane then owns one query (its column) and 16 of the 32 keys of each
+// MFMA tile, so the softmax max / sum need one cross-lane step (lane ^ 32).
+// The probabilities feed O^T = V^T P^T straight from the score registers:
+// a lane's eight keys of a 16-key PV step are the ones its score registers
+// hold (keys 0-3 and 8-11 of the group for the lower half-wave, 4-7 and
+// 12-15 for the upper), and V^T's operand is read in that key order with
+// gfx950's transposing LDS read (ds_read_b64_tr_b16: each lane of a 16-lane
+// group receives one column of a 4-key x 16-dim block whose rows the
+// group's lanes address, four keys of one dim), so P never moves between
+// lanes and V is never transposed in memory.
+//
+// Online softmax in base 2 with a running max and sum per query.  The
+// running max is raised only when some query's block max exceeds it by more
+// than PF_RESCALE_SLACK (then the accumulators are rescaled); otherwise the
+// probabilities of the block are exp2 of at most that slack, well inside
+// fp32 and bf16 range, and the final division by the row sum removes the
+// offset exactly as it removes the usual one.  The row sums take the
+// probabilities as rounded to bf16 for the PV product (a bf16 dot product
+// with ones), so numerator and denominator see the same values.  The output
+// tile is transposed through LDS so the [sum L, H] rows are written with
+// 16-byte stores.
+//
+// K/V rows are fetched with buffer loads whose resource starts at the
+// step's first key and ends at the block's last key: rows past it read as
+// zeros (their scores are masked), so no address is clamped per load.
+constexpr float PF_RESCALE_SLACK = 8.0f;
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+
+// transposing LDS read: lane j of each 16-lane group gets element (j % 4)
+// of the 4-element rows addressed by lanes 4k + (j % 16) / 4 of its group,
+// k = 0..3
+__device__ __forceinline__ s16x4_t lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p));
+}
+
+// a value of lane l and of lane l ^ 32 combined (gfx950's v_permlane32_swap
+// hands each half-wave the other half's value)
+__device__ __forceinline__ float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   constexpr int BQ = PREFILL_ROWS;       // 128 queries: 32 per wave
   constexpr int BKV = 64;                // keys per step
   constexpr int KLD = D + 8;             // K row stride (elements)
-  constexpr int VLD = BKV + 8;           // V^T row stride
+  // V row stride: rows 64 bytes apart modulo the 256-byte bank cycle, so a
+  // transposing read's eight key rows (64 bytes each) fill the banks twice
+  constexpr int VLD = D + 32;
   constexpr int OLD = D + 8;             // output staging row stride
-  constexpr int KV_ELEMS = BKV * KLD + D * VLD;
+  constexpr int K_ELEMS = BKV * KLD;
+  constexpr int STAGE = BKV * (KLD + VLD);
   constexpr int O_ELEMS = BQ * OLD;
-  // two K/V stages (the next step is written while this one is read)
-  constexpr int SMEM = 2 * KV_ELEMS > O_ELEMS ? 2 * KV_ELEMS : O_ELEMS;
+  constexpr int SMEM = 2 * STAGE > O_ELEMS ? 2 * STAGE : O_ELEMS;
+  static_assert((VLD / 2) % 16 == 0 && ((VLD / 2) / 16) % 2 == 1, "V stride");
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
 
   // grid (heads, items): all heads of the first (longest) item go first
@@ -255,63 +302,57 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
 
   // keys the block needs, and this wave (absolute positions, exclusive)
   const int kend = rq.kv_len + min(it.q1, it.q0 + BQ);
-  const int kend_wave = rq.kv_len + min(it.q1, it.q0 + w * 32 + 32);
-  const size_t head_base = ((size_t)h * a.cap + (size_t)rq.kv_base) * 2 * D;
-  const bf16* kb = (const bf16*)a.kv_pool + head_base;
-  const bf16* vb = kb + D;   // each slot's value row follows its key row
+  // (a wave whose 32 rows all lie past the chunk's end computes nothing)
+  const int kend_wave =
+      it.q0 + w * 32 < it.q1 ? rq.kv_len + min(it.q1, it.q0 + w * 32 + 32) : 0;
+  const bf16* kb =
+      (const bf16*)a.kv_pool + ((size_t)h * a.cap + (size_t)rq.kv_base) * 2 * D;
 
-  // K and V of the next 64-key step are loaded into registers while the
-  // current step runs on the MFMAs (16-byte loads; keys past the block's
-  // last one re-read it, so the loads never sit behind a branch)
-  constexpr int NL = BKV * (D / 8) / 256;   // 16-byte loads per thread, K and V each
-  static_assert(NL * 256 == BKV * (D / 8) && NL * 4 == D / 8, "tile not divisible by threads");
-  // vector-typed staging (not arrays) keeps the prefetch in registers
+  // K and V of the step after next are loaded into registers while the
+  // current step runs on the MFMAs.  Thread tid loads 16 bytes of key rows
+  // tid / (D/8) + (256 / (D/8)) i, at dims 8 (tid % (D/8)); the value row
+  // follows the key row in the pool (instruction offset 2D bytes).
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPP = 256 / CPR;             // rows per pass of the workgroup
+  constexpr int NL = BKV / RPP;              // passes per step (K and V each)
+  static_assert(NL * RPP == BKV, "tile not divisible by threads");
+  const int lrow = tid / CPR, lch = tid % CPR;
   typedef uint32_t Stage __attribute__((ext_vector_type(4 * NL)));
+  typedef uint32_t U4 __attribute__((ext_vector_type(4)));
   Stage kreg, vreg;
-  const int vkey = tid & 63;
-  // V^T column of key pair (vkey & ~1): bits 2 and 3 of the key swapped
-  // inside its 16-key group, the order in which a lane's P^T fragment holds
-  // its keys (4 half + 0..3, then 8 + 4 half + 0..3), so the lane's eight
-  // keys are one 16-byte read
-  const int vcol = (vkey & ~15) | (vkey & 2) | ((vkey & 4) << 1) | ((vkey & 8) >> 1);
-  // byte selectors of v_perm_b32 (bytes 0-3: second operand, 4-7: first):
-  // even key lanes take (own.lo16, neighbour.lo16), odd ones
-  // (neighbour.hi16, own.hi16)
-  const uint32_t vsel = (vkey & 1) ? 0x03020706u : 0x05040100u;
+  // the resource of a step covers keys k0 .. kend-1 (none past kend)
 #define ORCA_PF_LOAD(K0)                                                                     \
-  _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                           \
-    const int c = tid + 256 * i, key = c / (D / 8), ch = c % (D / 8);                        \
-    const uint4 tk = *reinterpret_cast<const uint4*>(                                        \
-        kb + (size_t)min((K0) + key, kend - 1) * 2 * D + ch * 8);                            \
-    const uint4 tv = *reinterpret_cast<const uint4*>(                                        \
-        vb + (size_t)min((K0) + vkey, kend - 1) * 2 * D + ((tid >> 6) + 4 * i) * 8);         \
-    kreg[4 * i] = tk.x; kreg[4 * i + 1] = tk.y; kreg[4 * i + 2] = tk.z; kreg[4 * i + 3] = tk.w; \
-    vreg[4 * i] = tv.x; vreg[4 * i + 1] = tv.y; vreg[4 * i + 2] = tv.z; vreg[4 * i + 3] = tv.w; \
-  }
-  // V^T: this lane holds dims d, d+1 of key vkey in each word; with the
-  // neighbouring key's word (lane ^ 1, a DPP move) an even lane writes row d
-  // (its own low half, then the neighbour's) and an odd lane row d+1 (the
-  // neighbour's high half, then its own), two consecutive keys per 32-bit
-  // store: one byte permute with a per-lane selector (a select between the
-  // two forms compiled to a divergent branch)
-#define ORCA_PF_STORE(BUF)                                                                   \
   {                                                                                          \
-    uint16_t* const stK = smem + (BUF) * KV_ELEMS;                                           \
-    uint16_t* const stV = stK + BKV * KLD;                                                   \
+    const int k0_ = (K0);                                                                    \
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(                     \
+        (void*)(kb + (size_t)k0_ * 2 * D), (short)0,                                         \
+        (int)((kend > k0_ ? kend - k0_ : 0) * 2 * D * 2), 0x00020000);                       \
     _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                         \
-      const int c = tid + 256 * i, key = c / (D / 8), ch = c % (D / 8);                      \
-      *reinterpret_cast<uint4*>(&stK[key * KLD + ch * 8]) =                                  \
-          make_uint4(kreg[4 * i], kreg[4 * i + 1], kreg[4 * i + 2], kreg[4 * i + 3]);        \
-      const int vch = (tid >> 6) + 4 * i;                                                    \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                        \
-        const uint32_t wv = vreg[4 * i + j];                                                 \
-        const uint32_t nb =                                                                  \
-            (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wv, 0xB1, 0xF, 0xF, false);       \
-        *reinterpret_cast<uint32_t*>(&stV[(vch * 8 + 2 * j + (vkey & 1)) * VLD + vcol]) =    \
-            __builtin_amdgcn_perm(nb, wv, vsel);                                             \
-      }                                                                                      \
+      const uint32_t off = (uint32_t)(((lrow + RPP * i) * 2 * D + lch * 8) * 2);             \
+      const U4 tk = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);                    \
+      const U4 tv = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 2 * D, 0, 0);            \
+      kreg[4 * i] = tk.x; kreg[4 * i + 1] = tk.y; kreg[4 * i + 2] = tk.z; kreg[4 * i + 3] = tk.w; \
+      vreg[4 * i] = tv.x; vreg[4 * i + 1] = tv.y; vreg[4 * i + 2] = tv.z; vreg[4 * i + 3] = tv.w; \
     }                                                                                        \
   }
+#define ORCA_PF_STORE(BUF)                                                                   \
+  {                                                                                          \
+    uint16_t* const stK = smem + (BUF) * STAGE;                                              \
+    uint16_t* const stV = stK + K_ELEMS;                                                     \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                         \
+      *reinterpret_cast<uint4*>(&stK[(lrow + RPP * i) * KLD + lch * 8]) =                    \
+          make_uint4(kreg[4 * i], kreg[4 * i + 1], kreg[4 * i + 2], kreg[4 * i + 3]);        \
+      *reinterpret_cast<uint4*>(&stV[(lrow + RPP * i) * VLD + lch * 8]) =                    \
+          make_uint4(vreg[4 * i], vreg[4 * i + 1], vreg[4 * i + 2], vreg[4 * i + 3]);        \
+    }                                                                                        \
+  }
+  // this lane's transposing-read row: key 4 half + (lane % 16) / 4 of a
+  // 16-key group, dims 16 ((lane / 16) % 2) + 4 (lane % 4) of a 32-dim block
+  const int g16 = lane & 15;
+  const int vtr = (4 * half + (g16 >> 2)) * VLD + 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+  const int kfr = col * KLD + half * 8;     // K fragment: key col, dims 8 half
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
   ORCA_PF_LOAD(0)
   ORCA_PF_STORE(0)
   ORCA_PF_LOAD(BKV)
@@ -325,91 +366,84 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     }
     ORCA_PF_LOAD(k0 + 2 * BKV)
     if (k0 < kend_wave) {
-    const uint16_t* sK = smem + cur * KV_ELEMS;
-    const uint16_t* sV = sK + BKV * KLD;
+      const uint16_t* sK = smem + cur * STAGE;
+      const uint16_t* sV = sK + K_ELEMS;
 
-    // S^T = K Q^T for keys k0 .. k0+63 (two 32-key tiles)
-    f32x16_t s[2];
+      // S^T = K Q^T for keys k0 .. k0+63 (two 32-key tiles)
+      f32x16_t s[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
+        for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8_t kf =
-            *reinterpret_cast<const bf16x8_t*>(&sK[(32 * t + col) * KLD + ks * 16 + half * 8]);
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
-      }
-    }
-    // causal mask, only on blocks reaching past the wave's first query or
-    // the last key (wave-uniform test); running max on the raw scores, the
-    // scale folded into the exponent below
-    // (the max and the sum below run as four independent chains, not one
-    // 32-deep dependent chain per lane)
-    float mq[4] = {NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
-    if (k0 + BKV - 1 <= qmin && k0 + BKV <= kend) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mq[r & 3] = fmaxf(mq[r & 3], s[t][r]);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = key <= qpos && key < kend;
-          s[t][r] = vis ? s[t][r] : NEG_BIG;
-          mq[r & 3] = fmaxf(mq[r & 3], s[t][r]);
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const bf16x8_t kf =
+              *reinterpret_cast<const bf16x8_t*>(&sK[kfr + 32 * t * KLD + ks * 16]);
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
         }
-    }
-    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // every query sees key 0 in the first block, so m_run is finite from
-    // then on and a masked score's exponent is far below it (p = 0)
-    // exponents are <= 0 here: the bare hardware exp2 (exact at 0; results
-    // below 2^-126 of the running max flush to zero, which no sum can see)
-    // instead of exp2f's range fix-up, five more instructions per score
-    const float m_new = fmaxf(m_run, mx * sc);
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= corr;
-    // once the running maxima settle, most steps leave every query's max
-    // unchanged (corr == 1): skip the rescale of the output accumulators
-    if (__any(corr != 1.f)) {
-#pragma unroll
-      for (int dm = 0; dm < D / 32; ++dm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dm][r] *= corr;
-    }
-    float lq[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], sc, -m_new));
-        s[t][r] = p;
-        lq[r & 3] += p;
       }
-    l_run += (lq[0] + lq[1]) + (lq[2] + lq[3]);
-    // O^T += V^T P^T, 16 keys per MFMA step
+      // causal mask, only on blocks reaching past the wave's first query or
+      // the last key (wave-uniform test); block max on the raw scores (the
+      // scale is positive and folded into the exponent below), four
+      // independent chains per lane
+      float mq[4] = {NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
+      if (k0 + BKV - 1 <= qmin && k0 + BKV <= kend) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int t = st >> 1, rb = (st & 1) * 8;
-      bf16x8_t pb;
-      {
-        uint32_t pk[4];
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(s[t][rb + 2 * j], s[t][rb + 2 * j + 1]);
-        pb = *reinterpret_cast<const bf16x8_t*>(pk);
+          for (int r = 0; r < 16; ++r) mq[r & 3] = fmaxf(mq[r & 3], s[t][r]);
+      } else {
+        // key k0 + 32 t + 8 (r / 4) + 4 half + r % 4 is visible when it is
+        // at most min(qpos, kend - 1)
+        const int lim = min(qpos, kend - 1) - k0 - 4 * half;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[t][r] = 32 * t + 8 * (r >> 2) + (r & 3) <= lim ? s[t][r] : NEG_BIG;
+            mq[r & 3] = fmaxf(mq[r & 3], s[t][r]);
+          }
       }
+      const float mx = halves_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]))) * sc;
+      // every query sees key 0 in the first block, so m_run is finite from
+      // then on; a masked score's exponent is far below it (p = 0)
+      if (__any(mx > m_run + PF_RESCALE_SLACK)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= corr;
 #pragma unroll
-      for (int dm = 0; dm < D / 32; ++dm) {
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(
-            &sV[(dm * 32 + col) * VLD + 16 * st + 8 * half]);
-        o[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[dm], 0, 0, 0);
+        for (int dm = 0; dm < D / 32; ++dm)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dm][r] *= corr;
       }
-    }
+      // exponents are <= PF_RESCALE_SLACK: the bare hardware exp2 (results
+      // below 2^-126 flush to zero, which no sum can see)
+      float lq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int t = st >> 1, rb = (st & 1) * 8;
+        bf16x8_t pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          pb[j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[t][rb + j], sc, -m_run));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2_t pp = {pb[2 * j], pb[2 * j + 1]};
+          lq[j] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lq[j], false);
+        }
+        // O^T += V^T P^T over the 16 keys of this step (k0 + 16 st ..)
+#pragma unroll
+        for (int dm = 0; dm < D / 32; ++dm) {
+          const uint16_t* vp = &sV[vtr + 16 * st * VLD + 32 * dm];
+          const s16x4_t v0 = lds_read_tr16(vp);
+          const s16x4_t v1 = lds_read_tr16(vp + 8 * VLD);
+          const bf16x8_t vf =
+              __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[dm], 0, 0, 0);
+        }
+      }
+      l_run += (lq[0] + lq[1]) + (lq[2] + lq[3]);
     }
     __syncthreads();
   }
@@ -417,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
 #undef ORCA_PF_LOAD
 #undef ORCA_PF_STORE
   // normalise, transpose through LDS, write the rows
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = halves_sum(l_run);
   const float inv = 1.f / l_tot;
   __syncthreads();
   uint16_t* sO = smem;
