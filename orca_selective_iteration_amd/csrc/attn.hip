@@ -31,6 +31,7 @@
 // HBM traffic of the split path per (row, head): 2 * keys * d * sizeof(T)
 // bytes of K and V, read once.
 #include <math.h>
+#include <stdlib.h>
 
 #include "device.h"
 #include "kernels.h"
@@ -200,9 +201,10 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 // Initiation rows of a bf16 model: causal attention of a prompt over itself.
 // A 256-thread workgroup takes one head and PREFILL_ROWS = 128 consecutive
 // query positions of one request (32 per wave) and walks the request's keys
-// 0 .. last query position in steps of 64.  Each step's K and V rows are
-// staged row-major in LDS (16-byte writes, two stages: the next step is
-// written while this one is read).
+// 0 .. last query position in steps of BKV (64 or 32; see
+// prefill_keys_per_step).  Each step's K and V rows are staged row-major in
+// LDS (16-byte writes, two stages: the next step is written while this one
+// is read).
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 // a lane then owns one query (its column) and 16 of the 32 keys of each
@@ -256,10 +258,10 @@ __device__ __forceinline__ float halves_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
+template <int D, int BKV, int WG_PER_CU>
+__global__ __launch_bounds__(256, WG_PER_CU) void attn_prefill_kernel(AttnArgs a) {
   constexpr int BQ = PREFILL_ROWS;       // 128 queries: 32 per wave
-  constexpr int BKV = 64;                // keys per step
+  constexpr int NT = BKV / 32;           // 32-key score tiles per step
   constexpr int KLD = D + 8;             // K row stride (elements)
   // V row stride: rows 64 bytes apart modulo the 256-byte bank cycle, so a
   // transposing read's eight key rows (64 bytes each) fill the banks twice
@@ -370,9 +372,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
       const uint16_t* sV = sK + K_ELEMS;
 
       // S^T = K Q^T for keys k0 .. k0+63 (two 32-key tiles)
-      f32x16_t s[2];
+      f32x16_t s[NT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < NT; ++t) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
 #pragma unroll
@@ -389,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
       float mq[4] = {NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
       if (k0 + BKV - 1 <= qmin && k0 + BKV <= kend) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mq[r & 3] = fmaxf(mq[r & 3], s[t][r]);
       } else {
@@ -397,7 +399,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
         // at most min(qpos, kend - 1)
         const int lim = min(qpos, kend - 1) - k0 - 4 * half;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             s[t][r] = 32 * t + 8 * (r >> 2) + (r & 3) <= lim ? s[t][r] : NEG_BIG;
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
       // below 2^-126 flush to zero, which no sum can see)
       float lq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      for (int st = 0; st < 2 * NT; ++st) {
         const int t = st >> 1, rb = (st & 1) * 8;
         bf16x8_t pb;
 #pragma unroll
@@ -472,6 +474,20 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   }
 }
 
+// Prefill form: 64-key steps with two workgroups per CU (~200 registers a
+// lane), or 32-key steps with three (~165 registers; 38 KB of LDS each).
+// Three per CU hide more of a step's latency but double the steps of every
+// tile, so they pay when the tiles are many (throughput-bound) and not when
+// the longest tile's chain of steps bounds the launch.  Measured (kernel
+// trace, MI355X): the 175B-layer prompt mix (8 prompts, 96 heads, 2,976
+// tiles) 110.6 -> 102 us with 32-key steps; two 1,024-token 13B prompts (40
+// heads, 640 tiles) 38.7 -> 40.5 us.  Above two rounds of two-per-CU slots
+// the 32-key form is taken.  ORCA_PF_KEYS (32 or 64) pins one, for tests.
+static int prefill_keys_per_step(int heads, int n_pf) {
+  if (const char* v = getenv("ORCA_PF_KEYS")) return atoi(v) == 32 ? 32 : 64;
+  return (long)heads * n_pf > 2L * 2 * 256 ? 32 : 64;
+}
+
 // Residency of the split-KV kernel.  Its registers allow four to five
 // 256-thread workgroups per CU, but the cache streams faster with two: fewer
 // K/V streams at once per HBM channel (measured: two per CU +0.7% at the
@@ -483,8 +499,14 @@ constexpr unsigned SPLIT_LDS_RESERVE = 60 * 1024;
 template <typename T, int D>
 static void launch_split(const AttnArgs& a, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (a.n_pf > 0)
-      hipLaunchKernelGGL((attn_prefill_kernel<D>), dim3(a.heads, a.n_pf), dim3(256), 0, s, a);
+    if (a.n_pf > 0) {
+      if (prefill_keys_per_step(a.heads, a.n_pf) == 32)
+        hipLaunchKernelGGL((attn_prefill_kernel<D, 32, 3>), dim3(a.heads, a.n_pf), dim3(256), 0, s,
+                           a);
+      else
+        hipLaunchKernelGGL((attn_prefill_kernel<D, 64, 2>), dim3(a.heads, a.n_pf), dim3(256), 0, s,
+                           a);
+    }
   }
   if (a.n_items == 0) return;
   hipLaunchKernelGGL((attn_split_kernel<T, D>), dim3(a.n_items, a.heads), dim3(256),

@@ -230,6 +230,28 @@ ATTN_CASES = [
 @pytest.mark.parametrize("dtype,hidden,heads,shape", ATTN_CASES)
 def test_split_attention(dtype, hidden, heads, shape):
     print(f"case attention {dtype} hidden={hidden} heads={heads} n={len(shape)}", flush=True)
+    _attention_case(dtype, hidden, heads, shape)
+
+
+# both prefill forms (64-key steps, two workgroups per CU; 32-key steps,
+# three per CU), pinned: whole prompts of 1-517 rows, prompt chunks over a
+# cached prefix (initiation rows with kv_len > 0), beside increments; head
+# dims 128 and 64
+PREFILL_CASES = [
+    (512, 4, [(517, 0), (200, 130), (65, 0), (1, 300), (2, 0), (31, 33), (129, 1), (64, 0)]),
+    (512, 8, [(300, 0), (97, 200), (1, 40), (33, 0), (128, 128)]),
+]
+
+
+@pytest.mark.parametrize("keys", ["64", "32"])
+@pytest.mark.parametrize("hidden,heads,shape", PREFILL_CASES)
+def test_prefill_forms(keys, hidden, heads, shape, monkeypatch):
+    print(f"case prefill keys={keys} hidden={hidden} heads={heads} n={len(shape)}", flush=True)
+    monkeypatch.setenv("ORCA_PF_KEYS", keys)
+    _attention_case("bf16", hidden, heads, shape)
+
+
+def _attention_case(dtype, hidden, heads, shape):
     rng = np.random.default_rng(hidden + heads + len(shape))
     q_len = [s[0] for s in shape]
     kv_len = [s[1] for s in shape]
