@@ -403,6 +403,44 @@ def decode_roofline(L, model, work, reps, log):
             "algorithmic_bytes": nbytes}
 
 
+def prefill_roofline(L, model, work, reps, log):
+    """Causal attention of the batch's prompts, timed inside iterations over
+    the initiation requests alone (their rows of the same input): the
+    engine's timing events around the attention step of every layer, which
+    then runs the prefill kernel only."""
+    import torch
+    pre = [i for i in range(work.n_reqs) if work.kv_len[i] == 0 and work.q_len[i] > 0]
+    if not pre or work.dtype != "bf16":
+        return None
+    H = work.hidden
+    full = model.descriptors()
+    rows = torch.cat([torch.arange(full[i][0], full[i][0] + work.q_len[i]) for i in pre])
+    x = model.x_bench.index_select(0, rows.to(model.x_bench.device))
+    y = torch.empty_like(x)
+    reqs = model.descriptors(reqs=pre)
+    model.iteration(reqs, x, y, model.stream)
+    L.orca_time_step(model.ctx, 1)      # ORCA_STEP_ATTENTION
+    vals = []
+    for _ in range(reps):
+        model.iteration(reqs, x, y, model.stream)
+        vals.append(sum(L.orca_step_times(model.ctx, work.layers)) / work.layers)
+    L.orca_time_step(model.ctx, -1)
+    vals.sort()
+    ms = vals[len(vals) // 2]
+    # causal Q K^T and P V: sum over prompts of 2 L (L + 1) H FLOP per layer
+    flops = sum(2.0 * work.q_len[i] * (work.q_len[i] + 1) * H for i in pre)
+    tflops = flops / (ms * 1e-3) / 1e12
+    tiles = sum((work.q_len[i] + 127) // 128 for i in pre) * work.heads
+    form = L.orca_op_prefill_keys(work.heads, tiles // work.heads)
+    log(f"  prefill attention ({len(pre)} prompts, {tiles} tiles, {form}-key steps): "
+        f"{ms * 1e3:.1f} us per layer, {tflops:.0f} TFLOP/s")
+    return {"bound": "mfma", "kernel": "attn_prefill_kernel (the batch's prompts, one layer, "
+            "timed inside iterations over the prompts alone)", "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "ms_per_launch": round(ms, 4),
+            "algorithmic_flops": flops, "tiles": tiles, "keys_per_step": form}
+
+
 def setup(name, seed):
     import torch
     from orca_selective_iteration_amd import synth
@@ -455,6 +493,7 @@ def run_workload(name, args, headline):
         if work.dtype == "bf16":
             out["roofline"] = gemm_roofline(L, model, work, args.step_reps, log)
             out["decode_attention"] = decode_roofline(L, model, work, args.kernel_reps, log)
+            out["prefill_attention"] = prefill_roofline(L, model, work, args.step_reps, log)
         if headline and not args.no_cpu_baseline:
             t1 = time.time()
             out["cpu_baseline"] = cpu_baseline(model, work)

@@ -269,6 +269,14 @@ size_t orca_op_linear_workspace_bytes(int32_t dtype, int32_t m, int32_t n, int32
  * forms; -1 for fp32 (the FMA kernel); -2 for shapes orca_op_linear
  * rejects. */
 int32_t orca_op_linear_variant(int32_t dtype, int32_t m, int32_t n, int32_t k);
+/* The form the prefill (initiation-row) attention of a bf16 model takes for
+ * `tiles` 128-query tiles per head over `heads` heads, without launching
+ * anything (host only): 64 (64-key steps, two workgroups per CU) or 32
+ * (32-key steps, three per CU, taken above two rounds of two-per-CU tiles,
+ * heads x tiles > 1024); the ORCA_PF_KEYS environment override (32 or 64)
+ * included.  -2 for heads < 1 or tiles < 0.  [houmin] 3.1.2: attention is
+ * computed per request; the form only changes how its tiles are scheduled. */
+int32_t orca_op_prefill_keys(int32_t heads, int32_t tiles);
 orca_status orca_op_linear(int32_t dtype, int32_t epilogue, const void* a, const void* w,
                            const void* bias, void* out, int32_t m, int32_t n, int32_t k,
                            void* workspace, size_t ws_bytes, void* stream);

@@ -483,7 +483,7 @@ __global__ __launch_bounds__(256, WG_PER_CU) void attn_prefill_kernel(AttnArgs a
 // tiles) 110.6 -> 102 us with 32-key steps; two 1,024-token 13B prompts (40
 // heads, 640 tiles) 38.7 -> 40.5 us.  Above two rounds of two-per-CU slots
 // the 32-key form is taken.  ORCA_PF_KEYS (32 or 64) pins one, for tests.
-static int prefill_keys_per_step(int heads, int n_pf) {
+int prefill_keys_per_step(int heads, int n_pf) {
   if (const char* v = getenv("ORCA_PF_KEYS")) return atoi(v) == 32 ? 32 : 64;
   return (long)heads * n_pf > 2L * 2 * 256 ? 32 : 64;
 }

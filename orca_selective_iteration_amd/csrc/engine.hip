@@ -502,6 +502,11 @@ int32_t orca_op_linear_variant(int32_t dtype, int32_t m, int32_t n, int32_t k) {
   return linear_plan_variant(dtype, m, n, k);
 }
 
+int32_t orca_op_prefill_keys(int32_t heads, int32_t tiles) {
+  if (heads < 1 || tiles < 0) return -2;
+  return prefill_keys_per_step(heads, tiles);
+}
+
 size_t orca_op_linear_workspace_bytes(int32_t dtype, int32_t m, int32_t n, int32_t k) {
   if (m < 0 || n < 64 || k < 64 || n % 64 || k % 64) return 0;
   return linear_workspace_bytes(dtype, m, n, k);

@@ -96,5 +96,8 @@ constexpr int SPLIT_CHUNK = 512;
 constexpr int PREFILL_ROWS = 128;
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// Keys per step of the prefill form a launch of `n_pf` tiles over `heads`
+// heads takes (64: two workgroups per CU; 32: three); ORCA_PF_KEYS pins it.
+int prefill_keys_per_step(int heads, int n_pf);
 
 }  // namespace orca

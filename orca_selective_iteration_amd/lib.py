@@ -84,6 +84,7 @@ def _declare(lib):
         "orca_op_layernorm": (c_int32, [I32, V, V, V, V, I32, I32, c_float, V]),
         "orca_op_linear_workspace_bytes": (S, [I32, I32, I32, I32]),
         "orca_op_linear_variant": (I32, [I32, I32, I32, I32]),
+        "orca_op_prefill_keys": (I32, [I32, I32]),
         "orca_op_linear": (c_int32, [I32, I32, V, V, V, V, I32, I32, I32, V, S, V]),
         "orca_op_linear_noalloc": (c_int32, [I32, I32, V, V, V, V, I32, I32, I32, V]),
         "orca_op_qkv": (c_int32, [I32, V, V, V, V, V, V, I32, I32, I32, I64, V, S, V]),
@@ -275,6 +276,10 @@ def orca_op_linear_workspace_bytes(dtype: int, m: int, n: int, k: int) -> int:
 
 def orca_op_linear_variant(dtype: int, m: int, n: int, k: int) -> int:
     return int(load().orca_op_linear_variant(dtype, m, n, k))
+
+
+def orca_op_prefill_keys(heads: int, tiles: int) -> int:
+    return int(load().orca_op_prefill_keys(heads, tiles))
 
 
 def orca_op_linear(dtype: int, epilogue: int, a, w, bias, out, m: int, n: int, k: int,

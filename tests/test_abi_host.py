@@ -289,6 +289,23 @@ def test_planner_variant(m, n, k, variant, monkeypatch):
     assert L.orca_op_linear_variant(L.ORCA_BF16, m, n, k) == variant
 
 
+# the prefill form (host only): 64-key steps, two workgroups per CU, up to two
+# rounds of tiles; 32-key steps, three per CU, above (13B: two 1,024-token
+# prompts over 40 heads, 16 tiles; the 175B-layer seed-0 mix: 31 tiles over
+# 96 heads)
+def test_prefill_form(monkeypatch):
+    monkeypatch.delenv("ORCA_PF_KEYS", raising=False)
+    assert L.orca_op_prefill_keys(40, 16) == 64
+    assert L.orca_op_prefill_keys(96, 31) == 32
+    assert L.orca_op_prefill_keys(16, 4) == 64
+    assert L.orca_op_prefill_keys(1024, 1) == 64 and L.orca_op_prefill_keys(1025, 1) == 32
+    monkeypatch.setenv("ORCA_PF_KEYS", "64")
+    assert L.orca_op_prefill_keys(96, 31) == 64
+    monkeypatch.setenv("ORCA_PF_KEYS", "32")
+    assert L.orca_op_prefill_keys(40, 16) == 32
+    assert L.orca_op_prefill_keys(0, 1) == -2 and L.orca_op_prefill_keys(4, -1) == -2
+
+
 def test_planner_variant_pin_and_rejects(monkeypatch):
     monkeypatch.setenv("ORCA_GEMM_VARIANT", "7")
     assert L.orca_op_linear_variant(L.ORCA_BF16, 2176, 20480, 5120) == 7
