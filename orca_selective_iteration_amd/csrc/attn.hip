@@ -322,13 +322,14 @@ __global__ __launch_bounds__(256, WG_PER_CU) void attn_prefill_kernel(AttnArgs a
   typedef uint32_t Stage __attribute__((ext_vector_type(4 * NL)));
   typedef uint32_t U4 __attribute__((ext_vector_type(4)));
   Stage kreg, vreg;
-  // the resource of a step covers keys k0 .. kend-1 (none past kend)
+  // the resource of a step covers its keys k0 .. min(k0 + BKV, kend) - 1
+  // (none past kend; at most BKV rows, so its size never nears 2^31)
 #define ORCA_PF_LOAD(K0)                                                                     \
   {                                                                                          \
     const int k0_ = (K0);                                                                    \
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(                     \
         (void*)(kb + (size_t)k0_ * 2 * D), (short)0,                                         \
-        (int)((kend > k0_ ? kend - k0_ : 0) * 2 * D * 2), 0x00020000);                       \
+        max(0, min(kend - k0_, BKV)) * 2 * D * 2, 0x00020000);                               \
     _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                         \
       const uint32_t off = (uint32_t)(((lrow + RPP * i) * 2 * D + lch * 8) * 2);             \
       const U4 tk = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);                    \
