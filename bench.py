@@ -592,6 +592,7 @@ def main():
         "config": head["config"],
         "roofline": head.get("roofline"),
         "decode_attention": head.get("decode_attention"),
+        "prefill_attention": head.get("prefill_attention"),
         "cpu_baseline": head.get("cpu_baseline"),
         "also": also or None,
     }
