@@ -229,13 +229,12 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 // tile is transposed through LDS so the [sum L, H] rows are written with
 // 16-byte stores.
 //
-// K/V rows are fetched with buffer loads whose resource starts at the
-// step's first key and ends at the block's last key: rows past it read as
-// zeros (their scores are masked), so no address is clamped per load.
+// K/V rows are fetched with buffer loads whose resource covers one step's
+// keys and ends at the block's last key: rows past it read as zeros (their
+// scores are masked), so no address is clamped per load.
 constexpr float PF_RESCALE_SLACK = 8.0f;
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
 // transposing LDS read: lane j of each 16-lane group gets element (j % 4)
 // of the 4-element rows addressed by lanes 4k + (j % 16) / 4 of its group,
