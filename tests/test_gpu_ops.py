@@ -164,6 +164,52 @@ def test_four_wave_is_deterministic(variant, monkeypatch):
     assert np.array_equal(outs[0], outs[1])
 
 
+# persistent four-wave launches (more than one round of tiles: one
+# workgroup per CU walks its XCD's share of them): the same bits as one
+# workgroup per tile (ORCA_GEMM_PERSIST=0; only the tile-to-workgroup
+# assignment differs), and sampled rows, the ragged last row tile among
+# them, against the oracle.  (1100, 20480, 256) on 256 x 256: 5 x 80 = 400
+# tiles, no tail; (1600, 15360, 512) on 256 x 192: 7 x 80 = 560 tiles;
+# (2176, 15360, 2048) on 256 x 256: 9 x 60 = 540 tiles = 512 persistent +
+# a 28-tile split-K tail.
+@pytest.mark.parametrize("m,n,k,variant,epi", [
+    (1100, 20480, 256, "12", L.ORCA_EPI_BIAS_GELU),
+    (1600, 15360, 512, "13", L.ORCA_EPI_BIAS),
+    (2176, 15360, 2048, "12", L.ORCA_EPI_BIAS_RESID)])
+def test_persistent_launch(m, n, k, variant, epi, monkeypatch):
+    print(f"case persistent m={m} n={n} k={k} variant={variant} epi={epi}", flush=True)
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", variant)
+    rng = np.random.default_rng(m + n + k)
+    a = draw(rng, (m, k), 1.0, "bf16")
+    w = draw(rng, (n, k), 0.02 * 32 / np.sqrt(k), "bf16")
+    b = draw(rng, n, 0.02, "bf16")
+    init = rng.standard_normal((m, n)).astype(np.float32)
+    nb = L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k)
+    ws = torch.empty(max(nb, 4), dtype=torch.uint8, device=DEV)
+    da, dw, db = dev(a, "bf16"), dev(w, "bf16"), dev(b, "bf16")
+    outs = []
+    for persist in ("1", "0"):
+        monkeypatch.setenv("ORCA_GEMM_PERSIST", persist)
+        if epi == L.ORCA_EPI_BIAS_RESID:
+            out = torch.from_numpy(init).to(DEV)
+        else:
+            out = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+        L.orca_op_linear(L.ORCA_BF16, epi, da, dw, db, out, m, n, k, ws, nb)
+        outs.append(out)
+    bits = [o.view(torch.int32 if o.dtype == torch.float32 else torch.int16).cpu().numpy()
+            for o in outs]
+    assert np.array_equal(bits[0], bits[1])
+    rows = np.array(sorted({0, 1, 255, 256, m // 2, m - 2, m - 1}))
+    ref = om.linear(a[rows].astype(np.float64), w.astype(np.float64), b.astype(np.float64))
+    if epi == L.ORCA_EPI_BIAS_RESID:
+        ref = init[rows].astype(np.float64) + ref
+    elif epi == L.ORCA_EPI_BIAS_GELU:
+        ref = om.gelu_tanh(ref)
+    got = host(outs[0])[rows]
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) < TOL["bf16"]
+
+
 def test_linear_empty_batch_is_noop():
     out = torch.full((4, 128), 3.0, device=DEV)
     a = torch.zeros((4, 64), device=DEV, dtype=torch.bfloat16)
