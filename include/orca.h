@@ -277,6 +277,23 @@ int32_t orca_op_linear_variant(int32_t dtype, int32_t m, int32_t n, int32_t k);
  * included.  -2 for heads < 1 or tiles < 0.  [houmin] 3.1.2: attention is
  * computed per request; the form only changes how its tiles are scheduled. */
 int32_t orca_op_prefill_keys(int32_t heads, int32_t tiles);
+/* The workgroup order of the prefill attention launch for a batch of a bf16
+ * model with `heads` heads, without launching anything (host only).  The
+ * batch's initiation requests (reqs[i].phase == ORCA_INITIATION) each
+ * contribute the 128-query tiles of their prompt rows; workgroup j of the
+ * launch computes the tile starting at query row q0_out[j] of request
+ * req_out[j] (an index into reqs) for head head_out[j].  Up to two rounds of
+ * two-per-CU workgroups (tiles x heads <= 1024): the tiles longest-first
+ * (by kv_len + last query row), the heads of a tile adjacent.  Beyond that:
+ * the tiles of each (request, head) together on one XCD (workgroup j runs
+ * on XCD j % 8), so they share its L2.  ORCA_PF_ORDER (0 or 1) pins either.
+ * Writes the first min(count, cap) entries (the arrays hold cap entries)
+ * and returns count = tiles x heads; -2 for n < 0, heads < 1, cap < 0,
+ * a negative q_len or kv_len, or missing arrays.  [houmin] 3.1.2:
+ * attention runs per request; the order only decides where and when its
+ * tiles run. */
+int32_t orca_op_prefill_order(const orca_req_desc* reqs, int32_t n, int32_t heads,
+                              int32_t* req_out, int32_t* q0_out, int32_t* head_out, int32_t cap);
 orca_status orca_op_linear(int32_t dtype, int32_t epilogue, const void* a, const void* w,
                            const void* bias, void* out, int32_t m, int32_t n, int32_t k,
                            void* workspace, size_t ws_bytes, void* stream);

@@ -33,6 +33,9 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "device.h"
 #include "kernels.h"
 #include "orca.h"
@@ -273,11 +276,13 @@ __global__ __launch_bounds__(256, WG_PER_CU) void attn_prefill_kernel(AttnArgs a
   static_assert((VLD / 2) % 16 == 0 && ((VLD / 2) / 16) % 2 == 1, "V stride");
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
 
-  // grid (heads, items): all heads of the first (longest) item go first
-  const PrefillItem it = a.pf[blockIdx.y];
-  const int h = blockIdx.x;
+  // workgroup i computes the tile and head of slot i (prefill_schedule)
+  const PrefillSlot sl = a.pf_slots[blockIdx.x];
+  const PrefillItem it = a.pf[sl.item];
+  const int h = sl.head;
   const DevReq rq = a.reqs[it.req];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // the wave (uniform)
   const int half = lane >> 5, col = lane & 31;
   const size_t H = (size_t)a.hidden;
 
@@ -322,13 +327,17 @@ __global__ __launch_bounds__(256, WG_PER_CU) void attn_prefill_kernel(AttnArgs a
   typedef uint32_t U4 __attribute__((ext_vector_type(4)));
   Stage kreg, vreg;
   // the resource of a step covers its keys k0 .. min(k0 + BKV, kend) - 1
-  // (none past kend; at most BKV rows, so its size never nears 2^31)
+  // (none past kend; at most BKV rows, so its size never nears 2^31).  Its
+  // size goes through readfirstlane: computed on the vector unit, it would
+  // not be known to be uniform, and every load would then be wrapped in a
+  // loop over the distinct resources of the wave (MI355X: 6% of the 13B
+  // prompts' prefill time, 5% of the 175B-layer mix's).
 #define ORCA_PF_LOAD(K0)                                                                     \
   {                                                                                          \
     const int k0_ = (K0);                                                                    \
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(                     \
         (void*)(kb + (size_t)k0_ * 2 * D), (short)0,                                         \
-        max(0, min(kend - k0_, BKV)) * 2 * D * 2, 0x00020000);                               \
+        __builtin_amdgcn_readfirstlane(max(0, min(kend - k0_, BKV)) * 2 * D * 2), 0x00020000); \
     _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                         \
       const uint32_t off = (uint32_t)(((lrow + RPP * i) * 2 * D + lch * 8) * 2);             \
       const U4 tk = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);                    \
@@ -488,6 +497,79 @@ int prefill_keys_per_step(int heads, int n_pf) {
   return (long)heads * n_pf > 2L * 2 * 256 ? 32 : 64;
 }
 
+// Order of a prefill launch's workgroups.  MI355X hands workgroup i to XCD
+// i % 8, each XCD with its own 4 MB L2, and every tile of one (request,
+// head) reads that head's keys and values from position 0 up.
+//  * Longest-first (up to two rounds of two-per-CU workgroups): workgroup i
+//    takes tile i / heads of the longest-first tile list and head i % heads,
+//    so the launch ends with its longest chain of key steps.
+//  * Grouped (more rounds): the (request, head) groups go, the requests with
+//    the most work first, to the XCD holding the fewest workgroups so far,
+//    each group's tiles one after another, so they run together and share
+//    their key/value reads through that XCD's L2; the lists are then evened
+//    out (XCD x takes the workgroups x, x + 8, ...).  MI355X, kernel trace:
+//    the 175B-layer prompt mix (8 prompts, 96 heads, 2,976 workgroups)
+//    103 -> 95 us, L2 fills 241 -> 122 MiB; over fewer rounds the groups
+//    that start last end the launch late (two 1,024-token 13B prompts, 640
+//    workgroups: 38.7 us longest-first, 48.9 grouped).
+bool prefill_grouped(int heads, int n_pf) {
+  if (const char* v = getenv("ORCA_PF_ORDER")) return atoi(v) == 1;
+  return (long)heads * n_pf > 2L * 2 * 256;
+}
+
+void prefill_schedule(const DevReq* reqs, int n_reqs, PrefillItem* pf, int n_pf, int heads,
+                      PrefillSlot* slots) {
+  // causal tiles cost ~ their last key position (cached prefix + last query)
+  auto end = [&](const PrefillItem& t) { return int64_t(reqs[t.req].kv_len) + t.q1; };
+  std::sort(pf, pf + n_pf, [&](const PrefillItem& a, const PrefillItem& b) {
+    const int64_t ea = end(a), eb = end(b);
+    return ea != eb ? ea > eb : (a.req != b.req ? a.req < b.req : a.q0 < b.q0);
+  });
+  const int n = n_pf * heads;
+  if (!prefill_grouped(heads, n_pf)) {
+    for (int i = 0; i < n; ++i) slots[i] = PrefillSlot{i / heads, i % heads};
+    return;
+  }
+  constexpr int NX = 8;   // XCDs
+  std::vector<std::vector<int>> tiles(n_reqs);
+  std::vector<int64_t> work(n_reqs, 0);
+  for (int k = 0; k < n_pf; ++k) {
+    tiles[pf[k].req].push_back(k);   // longest first
+    work[pf[k].req] += end(pf[k]);
+  }
+  std::vector<int> order;
+  for (int r = 0; r < n_reqs; ++r)
+    if (!tiles[r].empty()) order.push_back(r);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return work[a] > work[b]; });
+  std::vector<PrefillSlot> xs[NX];
+  int64_t xw[NX] = {};
+  for (int r : order)
+    for (int h = 0; h < heads; ++h) {
+      int x = 0;
+      for (int y = 1; y < NX; ++y)
+        if (xs[y].size() < xs[x].size() || (xs[y].size() == xs[x].size() && xw[y] < xw[x])) x = y;
+      for (int k : tiles[r]) xs[x].push_back(PrefillSlot{k, h});
+      xw[x] += work[r];
+    }
+  // even out the lists: XCD x takes the n / 8 (+1 for x < n % 8)
+  // workgroups x, x + 8, ...; surplus tiles (the shortest of the last
+  // groups) move to the XCDs short of theirs
+  std::vector<PrefillSlot> spill;
+  for (int x = 0; x < NX; ++x)
+    while ((int)xs[x].size() > n / NX + (x < n % NX)) {
+      spill.push_back(xs[x].back());
+      xs[x].pop_back();
+    }
+  for (int x = 0; x < NX; ++x) {
+    const int cnt = n / NX + (x < n % NX);
+    while ((int)xs[x].size() < cnt) {
+      xs[x].push_back(spill.back());
+      spill.pop_back();
+    }
+    for (int j = 0; j < cnt; ++j) slots[x + NX * j] = xs[x][j];
+  }
+}
+
 // Residency of the split-KV kernel.  Its registers allow four to five
 // 256-thread workgroups per CU, but the cache streams faster with two: fewer
 // K/V streams at once per HBM channel (measured: two per CU +0.7% at the
@@ -501,10 +583,10 @@ static void launch_split(const AttnArgs& a, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     if (a.n_pf > 0) {
       if (prefill_keys_per_step(a.heads, a.n_pf) == 32)
-        hipLaunchKernelGGL((attn_prefill_kernel<D, 32, 3>), dim3(a.heads, a.n_pf), dim3(256), 0, s,
+        hipLaunchKernelGGL((attn_prefill_kernel<D, 32, 3>), dim3(a.heads * a.n_pf), dim3(256), 0, s,
                            a);
       else
-        hipLaunchKernelGGL((attn_prefill_kernel<D, 64, 2>), dim3(a.heads, a.n_pf), dim3(256), 0, s,
+        hipLaunchKernelGGL((attn_prefill_kernel<D, 64, 2>), dim3(a.heads * a.n_pf), dim3(256), 0, s,
                            a);
     }
   }

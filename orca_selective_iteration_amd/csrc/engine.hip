@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
+#include <cstdint>
 #include <cstring>
 #include <new>
 #include <utility>
@@ -78,8 +80,10 @@ struct Plan {
   SplitItem* items;
   SplitRow* srows;
   PrefillItem* pf;
+  PrefillSlot* slots;
   int n_reqs = 0, rows = 0, n_items = 0, n_srows = 0, n_pf = 0;
-  size_t off_reqs = 0, off_row_dst = 0, off_items = 0, off_srows = 0, off_pf = 0, bytes = 0;
+  size_t off_reqs = 0, off_row_dst = 0, off_items = 0, off_srows = 0, off_pf = 0, off_slots = 0,
+         bytes = 0;
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -154,12 +158,14 @@ void build_plan(const orca_ctx* c, const orca_req_desc* reqs, int32_t n, int32_t
   p.off_items = take(sizeof(SplitItem) * n_items);
   p.off_srows = take(sizeof(SplitRow) * rows);
   p.off_pf = take(sizeof(PrefillItem) * n_pf);
+  p.off_slots = take(sizeof(PrefillSlot) * n_pf * c->desc.heads);
   p.bytes = o;
   p.reqs = reinterpret_cast<DevReq*>(buf + p.off_reqs);
   p.row_dst = reinterpret_cast<int32_t*>(buf + p.off_row_dst);
   p.items = reinterpret_cast<SplitItem*>(buf + p.off_items);
   p.srows = reinterpret_cast<SplitRow*>(buf + p.off_srows);
   p.pf = reinterpret_cast<PrefillItem*>(buf + p.off_pf);
+  p.slots = reinterpret_cast<PrefillSlot*>(buf + p.off_slots);
   p.n_reqs = n;
   p.rows = rows;
   int ni = 0, ns = 0, np = 0;
@@ -185,14 +191,8 @@ void build_plan(const orca_ctx* c, const orca_req_desc* reqs, int32_t n, int32_t
   p.n_items = ni;
   p.n_srows = ns;
   p.n_pf = np;
-  // causal prefill tiles cost ~ their last key position (cached prefix +
-  // last query): dispatch the longest first so the short ones fill in
-  // behind them
-  const DevReq* dr = p.reqs;
-  std::sort(p.pf, p.pf + np, [dr](const PrefillItem& a, const PrefillItem& b) {
-    const int64_t ea = int64_t(dr[a.req].kv_len) + a.q1, eb = int64_t(dr[b.req].kv_len) + b.q1;
-    return ea != eb ? ea > eb : (a.req != b.req ? a.req < b.req : a.q0 < b.q0);
-  });
+  // the tiles longest-first and the workgroup order of the prefill launch
+  prefill_schedule(p.reqs, n, p.pf, np, c->desc.heads, p.slots);
 }
 
 orca_status hip_fail(hipError_t e, const char* what) {
@@ -237,6 +237,7 @@ orca_status stage(orca_ctx* c, const orca_req_desc* reqs, int32_t n, char* ws, h
   aa.srows = reinterpret_cast<const SplitRow*>(dev + p.off_srows);
   aa.n_srows = p.n_srows;
   aa.pf = reinterpret_cast<const PrefillItem*>(dev + p.off_pf);
+  aa.pf_slots = reinterpret_cast<const PrefillSlot*>(dev + p.off_slots);
   aa.n_pf = p.n_pf;
   aa.part_o = reinterpret_cast<float*>(ws + c->off_part_o);
   aa.part_ml = reinterpret_cast<float*>(ws + c->off_part_ml);
@@ -317,7 +318,8 @@ orca_status orca_create(const orca_model_desc* desc, const orca_layer_weights* l
   c->off_gpart = take(c->gpart_bytes);
   c->meta_bytes = sizeof(DevReq) * max_reqs + sizeof(int32_t) * R +
                   sizeof(SplitItem) * c->max_items + sizeof(SplitRow) * R +
-                  sizeof(PrefillItem) * c->max_pf + 16 * 8;
+                  sizeof(PrefillItem) * c->max_pf + sizeof(PrefillSlot) * c->max_pf * d.heads +
+                  16 * 9;
   c->off_meta = take(c->meta_bytes);
   c->ws_bytes = o;
   hipError_t e = hipGetDevice(&c->device);
@@ -505,6 +507,33 @@ int32_t orca_op_linear_variant(int32_t dtype, int32_t m, int32_t n, int32_t k) {
 int32_t orca_op_prefill_keys(int32_t heads, int32_t tiles) {
   if (heads < 1 || tiles < 0) return -2;
   return prefill_keys_per_step(heads, tiles);
+}
+
+int32_t orca_op_prefill_order(const orca_req_desc* reqs, int32_t n, int32_t heads,
+                              int32_t* req_out, int32_t* q0_out, int32_t* head_out, int32_t cap) {
+  if (n < 0 || heads < 1 || cap < 0 || (n > 0 && !reqs)) return -2;
+  std::vector<DevReq> dr(n);
+  std::vector<PrefillItem> pf;
+  for (int i = 0; i < n; ++i) {
+    const orca_req_desc& r = reqs[i];
+    if (r.q_len < 0 || r.kv_len < 0) return -2;
+    dr[i] = DevReq{r.q_offset, r.q_len, r.kv_len, r.phase, r.kv_base};
+    if (r.phase == ORCA_INITIATION)
+      for (int q0 = 0; q0 < r.q_len; q0 += PREFILL_ROWS)
+        pf.push_back(PrefillItem{i, q0, std::min(r.q_len, q0 + PREFILL_ROWS), 0});
+  }
+  const int64_t total = int64_t(pf.size()) * heads;
+  if (total > INT32_MAX) return -2;
+  std::vector<PrefillSlot> slots(total);
+  prefill_schedule(dr.data(), n, pf.data(), int(pf.size()), heads, slots.data());
+  if (cap > 0 && (!req_out || !q0_out || !head_out)) return -2;
+  for (int64_t i = 0; i < std::min<int64_t>(total, cap); ++i) {
+    const PrefillItem& t = pf[slots[i].item];
+    req_out[i] = t.req;
+    q0_out[i] = t.q0;
+    head_out[i] = slots[i].head;
+  }
+  return int32_t(total);
 }
 
 size_t orca_op_linear_workspace_bytes(int32_t dtype, int32_t m, int32_t n, int32_t k) {

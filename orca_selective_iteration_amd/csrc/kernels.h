@@ -75,6 +75,11 @@ struct SplitRow {
 struct PrefillItem {
   int32_t req, q0, q1, pad;
 };
+// One workgroup of a prefill launch: tile `item` (an index into the prefill
+// items) for head `head`.
+struct PrefillSlot {
+  int32_t item, head;
+};
 
 struct AttnArgs {
   int dtype, hidden, heads, head_dim;
@@ -86,6 +91,7 @@ struct AttnArgs {
   const SplitItem* items;  int n_items;
   const SplitRow* srows;   int n_srows;
   const PrefillItem* pf;   int n_pf;
+  const PrefillSlot* pf_slots;   // [n_pf * heads]: what workgroup i computes
   float* part_o;          // [n_items][heads][d]
   float* part_ml;         // [n_items][heads][2]
 };
@@ -99,5 +105,13 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // Keys per step of the prefill form a launch of `n_pf` tiles over `heads`
 // heads takes (64: two workgroups per CU; 32: three); ORCA_PF_KEYS pins it.
 int prefill_keys_per_step(int heads, int n_pf);
+// Order of a prefill launch's workgroups: false, the tiles longest-first
+// with the heads of one tile adjacent; true, grouped by (request, head) per
+// XCD (prefill_schedule); ORCA_PF_ORDER (0 or 1) pins it.
+bool prefill_grouped(int heads, int n_pf);
+// Fills slots[0 .. n_pf * heads) for the prefill tiles pf[0 .. n_pf) of
+// requests reqs, sorting pf longest-first (by cached prefix + last query).
+void prefill_schedule(const DevReq* reqs, int n_reqs, PrefillItem* pf, int n_pf, int heads,
+                      PrefillSlot* slots);
 
 }  // namespace orca

@@ -85,6 +85,8 @@ def _declare(lib):
         "orca_op_linear_workspace_bytes": (S, [I32, I32, I32, I32]),
         "orca_op_linear_variant": (I32, [I32, I32, I32, I32]),
         "orca_op_prefill_keys": (I32, [I32, I32]),
+        "orca_op_prefill_order": (I32, [POINTER(orca_req_desc), I32, I32, POINTER(I32),
+                                        POINTER(I32), POINTER(I32), I32]),
         "orca_op_linear": (c_int32, [I32, I32, V, V, V, V, I32, I32, I32, V, S, V]),
         "orca_op_linear_noalloc": (c_int32, [I32, I32, V, V, V, V, I32, I32, I32, V]),
         "orca_op_qkv": (c_int32, [I32, V, V, V, V, V, V, I32, I32, I32, I64, V, S, V]),
@@ -280,6 +282,19 @@ def orca_op_linear_variant(dtype: int, m: int, n: int, k: int) -> int:
 
 def orca_op_prefill_keys(heads: int, tiles: int) -> int:
     return int(load().orca_op_prefill_keys(heads, tiles))
+
+
+def orca_op_prefill_order(reqs, heads: int):
+    """(req, q0, head) of each workgroup of the prefill launch, in launch
+    order; raises OrcaError on arguments the library rejects."""
+    arr = req_array(reqs)
+    n = len(reqs)
+    count = int(load().orca_op_prefill_order(arr, n, heads, None, None, None, 0))
+    if count < 0:
+        raise OrcaError(ORCA_ERR_INVALID, "orca_op_prefill_order", "invalid arguments")
+    r, q, h = ((c_int32 * max(count, 1))() for _ in range(3))
+    load().orca_op_prefill_order(arr, n, heads, r, q, h, count)
+    return [(r[i], q[i], h[i]) for i in range(count)]
 
 
 def orca_op_linear(dtype: int, epilogue: int, a, w, bias, out, m: int, n: int, k: int,

@@ -306,6 +306,83 @@ def test_prefill_form(monkeypatch):
     assert L.orca_op_prefill_keys(0, 1) == -2 and L.orca_op_prefill_keys(4, -1) == -2
 
 
+# the prefill launch's workgroup order (host only).  Every (tile, head) of
+# the batch's initiation requests appears once.  Up to two rounds of
+# two-per-CU workgroups the tiles run longest-first (by cached prefix + last
+# query row) with the heads of one tile adjacent; beyond, each (request,
+# head)'s tiles sit on one XCD (workgroup j on XCD j % 8), the XCDs take
+# equal workgroup counts, and their work (sum of tile ends) is balanced.
+def _prefill_batch(rng, n):
+    reqs, off = [], 0
+    for _ in range(n):
+        phase = L.ORCA_INITIATION if rng.random() < 0.7 else L.ORCA_INCREMENT
+        q = int(rng.integers(1, 1100)) if phase == L.ORCA_INITIATION else 1
+        kv = int(rng.integers(0, 600)) if rng.random() < 0.3 else 0
+        reqs.append((off, q, kv, phase, 0))
+        off += q
+    return reqs
+
+
+def _prefill_tiles(reqs):
+    return [(i, q0, r[2] + min(r[1], q0 + 128)) for i, r in enumerate(reqs)
+            if r[3] == L.ORCA_INITIATION for q0 in range(0, r[1], 128)]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefill_order(seed, monkeypatch):
+    monkeypatch.delenv("ORCA_PF_ORDER", raising=False)
+    rng = np.random.default_rng(300 + seed)
+    reqs = _prefill_batch(rng, int(rng.integers(1, 12)))
+    tiles = _prefill_tiles(reqs)
+    end = {(r, q0): e for r, q0, e in tiles}
+    heads = int(rng.integers(1, 130))
+    got = L.orca_op_prefill_order(reqs, heads)
+    assert sorted(got) == sorted((r, q0, h) for r, q0, _ in tiles for h in range(heads))
+    if len(tiles) * heads <= 1024:
+        ends = [end[(r, q0)] for r, q0, h in got]
+        assert ends == sorted(ends, reverse=True)
+        assert [h for _, _, h in got] == [j % heads for j in range(len(got))]
+        return
+    n = len(got)
+    xcd = {}
+    for j, (r, q0, h) in enumerate(got):
+        xcd.setdefault((r, h), set()).add(j % 8)
+    # only the tiles moved to even out the counts leave their group's XCD
+    split = sum(len(v) > 1 for v in xcd.values())
+    assert split <= 8, split
+    work = [0] * 8
+    for j, (r, q0, h) in enumerate(got):
+        work[j % 8] += end[(r, q0)]
+    biggest = max(sum(end[(r, q0)] for q0 in range(0, reqs[r][1], 128)) for r, _, _ in tiles)
+    assert max(work) - min(work) <= 2 * biggest
+
+
+def test_prefill_order_forms(monkeypatch):
+    monkeypatch.delenv("ORCA_PF_ORDER", raising=False)
+    # the 175B-layer seed-0 prompt mix over 96 heads: grouped; two
+    # 1,024-token prompts over 40 heads: longest-first
+    mix = [891, 699, 586, 369, 404, 164, 195, 142]
+    reqs = [(0, q, 0, L.ORCA_INITIATION, 0) for q in mix]
+    got = L.orca_op_prefill_order(reqs, 96)
+    assert len(got) == 31 * 96
+    assert {j % 8 for j, (r, q0, h) in enumerate(got) if (r, h) == (0, 5)} == {got.index((0, 0, 5)) % 8}
+    two = [(0, 1024, 0, L.ORCA_INITIATION, 0), (1024, 1024, 0, L.ORCA_INITIATION, 0)]
+    got = L.orca_op_prefill_order(two, 40)
+    assert got[:3] == [(0, 896, 0), (0, 896, 1), (0, 896, 2)] and got[40] == (1, 896, 0)
+    monkeypatch.setenv("ORCA_PF_ORDER", "1")
+    got = L.orca_op_prefill_order(two, 40)
+    assert len({j % 8 for j, (r, q0, h) in enumerate(got) if (r, h) == (1, 7)}) == 1
+    monkeypatch.setenv("ORCA_PF_ORDER", "0")
+    got = L.orca_op_prefill_order(reqs, 96)
+    assert got[:2] == [(0, 768, 0), (0, 768, 1)]
+    # increments take no prefill tile; invalid arguments
+    assert L.orca_op_prefill_order([(0, 1, 5, L.ORCA_INCREMENT, 0)], 8) == []
+    with pytest.raises(L.OrcaError):
+        L.orca_op_prefill_order(two, 0)
+    with pytest.raises(L.OrcaError):
+        L.orca_op_prefill_order([(0, -1, 0, L.ORCA_INITIATION, 0)], 4)
+
+
 def test_planner_variant_pin_and_rejects(monkeypatch):
     monkeypatch.setenv("ORCA_GEMM_VARIANT", "7")
     assert L.orca_op_linear_variant(L.ORCA_BF16, 2176, 20480, 5120) == 7
