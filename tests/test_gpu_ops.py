@@ -169,11 +169,13 @@ def test_four_wave_is_deterministic(variant, monkeypatch):
 # workgroup per tile (ORCA_GEMM_PERSIST=0; only the tile-to-workgroup
 # assignment differs), and sampled rows, the ragged last row tile among
 # them, against the oracle.  (1100, 20480, 256) on 256 x 256: 5 x 80 = 400
-# tiles, no tail; (1600, 15360, 512) on 256 x 192: 7 x 80 = 560 tiles;
-# (2176, 15360, 2048) on 256 x 256: 9 x 60 = 540 tiles = 512 persistent +
-# a 28-tile split-K tail.
+# tiles, no tail; (1100, 20224, 256): 5 x 79 = 395 tiles, not a multiple of
+# the 8 XCDs (three XCDs take one tile more); (1600, 15360, 512) on 256 x
+# 192: 7 x 80 = 560 tiles; (2176, 15360, 2048) on 256 x 256: 9 x 60 = 540
+# tiles = 512 persistent + a 28-tile split-K tail.
 @pytest.mark.parametrize("m,n,k,variant,epi", [
     (1100, 20480, 256, "12", L.ORCA_EPI_BIAS_GELU),
+    (1100, 20224, 256, "12", L.ORCA_EPI_BIAS),
     (1600, 15360, 512, "13", L.ORCA_EPI_BIAS),
     (2176, 15360, 2048, "12", L.ORCA_EPI_BIAS_RESID)])
 def test_persistent_launch(m, n, k, variant, epi, monkeypatch):
@@ -289,11 +291,17 @@ PREFILL_CASES = [
 ]
 
 
+# both forms and both workgroup orders (longest-first; grouped by (request,
+# head) per XCD) on whole prompts and chunks: the order only moves where a
+# tile runs, so every output row must match the oracle either way
+@pytest.mark.parametrize("order", ["0", "1"])
 @pytest.mark.parametrize("keys", ["64", "32"])
 @pytest.mark.parametrize("hidden,heads,shape", PREFILL_CASES)
-def test_prefill_forms(keys, hidden, heads, shape, monkeypatch):
-    print(f"case prefill keys={keys} hidden={hidden} heads={heads} n={len(shape)}", flush=True)
+def test_prefill_forms(keys, order, hidden, heads, shape, monkeypatch):
+    print(f"case prefill keys={keys} order={order} hidden={hidden} heads={heads} "
+          f"n={len(shape)}", flush=True)
     monkeypatch.setenv("ORCA_PF_KEYS", keys)
+    monkeypatch.setenv("ORCA_PF_ORDER", order)
     _attention_case("bf16", hidden, heads, shape)
 
 
