@@ -674,13 +674,16 @@ constexpr int W4_THREADS = 256;
 // modulo the bank cycle: the writes are conflict-free), then every thread
 // stores 16-byte pieces of whole rows: a store instruction covers 1 KB of
 // two to three rows, where the accumulator layout gives 32 rows x 16 bytes.
-// Same values, same bits as the direct epilogue.  MI355X, in-iteration:
-// FFN1 -2.5% (175B layer and 13B), the 175B layer's QKV projection -2.7%.
+// Same values, same bits as the direct epilogue.  MI355X, in-iteration,
+// same box: FFN1 -1.6% (175B layer) and -1.9% (13B), the 175B layer's QKV
+// projection -2.4%.
 // Measured and not taken: the fp32 residual epilogue staged in two halves
-// of 128 rows (175B output projection +1.9%, FFN2 and the 13B shapes
-// unchanged), and the QKV projection on the 256 x 192 tile, whose 24
-// pieces a row do not divide the workgroup, so each piece looks up its
-// head block (+1.6%).
+// of 128 rows (175B output projection +1.9% with 8 residual pieces in
+// flight per thread, +1.2% with 16, +5% with 32; the 13B output projection
+// -1.4%; FFN2 unchanged), and the QKV projection on the 256 x 192 tile,
+// whose 24 pieces a row do not divide the workgroup (each piece looking up
+// its head block: +1.6%; 192 threads keeping one piece's column each: no
+// faster).
 template <int EPI, int TJ>
 __device__ __forceinline__ void store_tile_staged(const f32x16_t (&acc)[4][TJ],
                                                   const bf16* __restrict__ bias,
