@@ -684,6 +684,45 @@ constexpr int W4_THREADS = 256;
 // whose 24 pieces a row do not divide the workgroup (each piece looking up
 // its head block: +1.6%; 192 threads keeping one piece's column each: no
 // faster).
+// The fp32 partial sums of a split-tail tile into its dense [BM][BN] block,
+// staged through LDS in two halves of 128 rows (row stride BN + 4 floats),
+// then stored as 16-byte pieces of whole rows: the block is contiguous, so
+// a store instruction covers 1 KB.  It also frees the registers the direct
+// store spilled.  MI355X, 175B layer in-iteration (three alternations):
+// QKV and FFN1 with their tails -0.3%.
+template <int TJ>
+__device__ __forceinline__ void store_partial_staged(const f32x16_t (&acc)[4][TJ], float* dst,
+                                                     int wm, int wn, int lane, int tid,
+                                                     uint16_t* smem) {
+  constexpr int TI = 4, BN = 64 * TJ, SLD = BN + 4, HM = 128, CPF = BN / 4;
+  static_assert(HM * SLD * 4 <= (2 * 256 * LDK + 2 * BN * LDK) * 2, "half a tile fits");
+  float* const sF = reinterpret_cast<float*>(smem);
+  const int mr = lane & 31, nh = (lane >> 5) * 4, c0 = wn * 32 * TJ;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    __syncthreads();   // the last fragment reads, or the last half's LDS reads, are done
+    if (wm == hf) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(&sF[(32 * i + mr) * SLD + c0 + 32 * j + 8 * q + nh]) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]);
+    }
+    __syncthreads();
+    float* const out = dst + (size_t)hf * HM * BN;
+#pragma unroll 4
+    for (int idx = tid; idx < HM * CPF; idx += W4_THREADS) {
+      const int r = idx / CPF, c = idx - r * CPF;
+      *reinterpret_cast<float4*>(out + (size_t)r * BN + 4 * c) =
+          *reinterpret_cast<const float4*>(&sF[r * SLD + 4 * c]);
+    }
+  }
+}
+
 template <int EPI, int TJ>
 __device__ __forceinline__ void store_tile_staged(const f32x16_t (&acc)[4][TJ],
                                                   const bf16* __restrict__ bias,
@@ -760,12 +799,13 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
   constexpr int TI = 4, BM = 256, BN = 64 * TJ;
   // 16-byte chunks per lane and K step: LA of A rows, then LB of W rows
   constexpr int LA = BM * 8 / W4_THREADS, LB = BN * 8 / W4_THREADS, NC = LA + LB;
-  // the two K-step stages.  The staged bf16 epilogues lay them out in one
-  // buffer, which holds the output tile after the K loop; the other
-  // epilogues keep two arrays (one buffer costs their register allocation
-  // more spills; only the variable a form uses is allocated)
+  // the two K-step stages.  The staged epilogues (bf16 outputs and the
+  // split tail's partial sums) lay them out in one buffer, which holds the
+  // output tile after the K loop; the residual epilogue keeps two arrays
+  // (one buffer costs its register allocation more spills; only the
+  // variables a form uses are allocated)
   constexpr bool STAGED = EPI == ORCA_EPI_BIAS || EPI == ORCA_EPI_BIAS_GELU ||
-                          (EPI == EPI_QKV && TJ == 4);
+                          (EPI == EPI_QKV && TJ == 4) || EPI == EPI_PARTIAL;
   __shared__ __attribute__((aligned(16))) uint16_t smem_w4[2 * BM * LDK + 2 * BN * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sA_w4[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sB_w4[2][BN * LDK];
@@ -955,8 +995,7 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
       pe.out = static_cast<float*>(ep.out) +
                ((size_t)blockIdx.y * map.n_tail + local) * BM * BN;
       pe.ldo = BN;
-      store_wave_tile_t<EPI, TI, TJ>(acc, bias, pe, M - tm * BM, N - tn * BN, wm * 32 * TI,
-                                     wn * 32 * TJ, lane);
+      store_partial_staged<TJ>(acc, static_cast<float*>(pe.out), wm, wn, lane, tid, smem_w4);
     } else if constexpr (STAGED) {
       store_tile_staged<EPI, TJ>(acc, bias, ep, M, N, tm, tn, wm, wn, lane, tid, smem_w4);
     } else {
