@@ -147,7 +147,39 @@ struct TileMap {
   // (from tile_base), each XCD a contiguous share of them, its workgroups
   // walking it in strides of one round; 0: one tile per workgroup
   int persist;
+  // > 0: a main-and-helper tail, a tile's K steps (see sk_segment); 0: the
+  // tail's K is split evenly over grid.y
+  int sk_kt;
 };
+
+// Main-and-helper tail (a form of stream-K): gridDim.x = NUM_CU workgroups
+// share the n_tail tail tiles.  Workgroup g < n_tail (logical) is tile g's
+// main: K steps [0, x), x = kt_per_split.  The other gridDim.x - n_tail are
+// helpers: helper h takes steps [x, sk_kt) of tiles h, h + helpers, ...
+// Mains run the same K steps of neighbouring tiles at the same time, and so
+// do the helpers, so an XCD's workgroups share A and W panels through its
+// L2 as in a full round.  (Contiguous ranges of the tiles' K steps laid end
+// to end balance exactly but leave every workgroup at its own K offset: on
+// the 175B-layer FFN2 that read ~10 GB for the round and ran 0.3 ms slower
+// than no tail.)  Tile t's partial sums: slot t (main), n_tail + t (helper).
+__device__ __forceinline__ int sk_segments(const TileMap& m, int g) {
+  const int helpers = gridDim.x - m.n_tail, h = g - m.n_tail;
+  return g < m.n_tail ? 1 : (m.n_tail - h + helpers - 1) / helpers;
+}
+__device__ __forceinline__ void sk_segment(const TileMap& m, int g, int seg, int& tile, int& k0,
+                                           int& kt, size_t& slot) {
+  if (g < m.n_tail) {
+    tile = g;
+    k0 = 0;
+    kt = m.kt_per_split;
+    slot = g;
+  } else {
+    tile = g - m.n_tail + seg * (gridDim.x - m.n_tail);
+    k0 = m.kt_per_split;
+    kt = m.sk_kt - m.kt_per_split;
+    slot = (size_t)m.n_tail + tile;
+  }
+}
 
 // Workgroup tile (WGM*32*TI) x (WGN*32*TJ): a WGM x WGN grid of waves, each
 // owning (32*TI) x (32*TJ) outputs as TI x TJ 32x32 MFMA accumulators.
@@ -817,9 +849,11 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  // this workgroup's K steps: [k0, k0 + KT) (all of K outside a split tail)
-  const int k0 = blockIdx.y * map.kt_per_split;
-  const int KT = min(K / BK - k0, map.kt_per_split);
+  // this workgroup's K steps: all of K outside a split tail.  A tail
+  // workgroup sets its K range per tile below (KT steps from the byte
+  // offset koff into the unshifted operands)
+  const int k0 = EPI == EPI_PARTIAL ? 0 : blockIdx.y * map.kt_per_split;
+  const int KT_all = min(K / BK - k0, map.kt_per_split);
   A += (size_t)k0 * BK;
   W += (size_t)k0 * BK;
 
@@ -855,7 +889,7 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
 // chunk c of a stage: c < LA are A rows, the rest W rows
 #define ORCA_W4_LOAD(S, KS, C0, C1)                                                           \
   {                                                                                           \
-    const int kb = (KS) * BK * 2;                                                             \
+    const int kb = (KS) * BK * 2 + koff;                                                      \
     _Pragma("unroll") for (int c = (C0); c < (C1); ++c) {                                     \
       const U4 t = c < LA ? __builtin_amdgcn_raw_buffer_load_b128(rA, offA[c], kb, 0)         \
                           : __builtin_amdgcn_raw_buffer_load_b128(rB, offB[c - LA], kb, 0);   \
@@ -951,10 +985,23 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
   } else {
     t_first = xcd_remap(blockIdx.x, gridDim.x);
     t_stride = 1;
-    t_count = 1;
+    t_count = EPI == EPI_PARTIAL && map.sk_kt > 0 ? sk_segments(map, t_first) : 1;
   }
   for (int it = 0; it < t_count; ++it) {
-    const int local = t_first + it * t_stride;
+    int local = t_first + it * t_stride, KT = KT_all, koff = 0;
+    size_t slot = 0;   // a tail tile's fp32 partial tile
+    if constexpr (EPI == EPI_PARTIAL) {
+      if (map.sk_kt > 0) {
+        int kfirst;
+        sk_segment(map, t_first, it, local, kfirst, KT, slot);
+        koff = kfirst * BK * 2;
+      } else {
+        const int kfirst = blockIdx.y * map.kt_per_split;
+        KT = min(K / BK - kfirst, map.kt_per_split);
+        koff = kfirst * BK * 2;
+        slot = (size_t)blockIdx.y * map.n_tail + local;
+      }
+    }
     int tm, tn;
     tile_of(map.tile_base + local, map.tiles_m, map.ntiles, map.group, tm, tn);
 #pragma unroll
@@ -990,12 +1037,10 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
 #undef ORCA_W4_LOAD
 #undef ORCA_W4_STORE
     if constexpr (EPI == EPI_PARTIAL) {
-      // split tail: this split's sums of the tile, [split][tail tile][BM][BN]
-      EpiParams pe = ep;
-      pe.out = static_cast<float*>(ep.out) +
-               ((size_t)blockIdx.y * map.n_tail + local) * BM * BN;
-      pe.ldo = BN;
-      store_partial_staged<TJ>(acc, static_cast<float*>(pe.out), wm, wn, lane, tid, smem_w4);
+      // split tail: this workgroup's sums of the tile into its partial tile
+      // (split-major for an even split; main, then helper, parts)
+      store_partial_staged<TJ>(acc, static_cast<float*>(ep.out) + slot * BM * BN, wm, wn, lane,
+                               tid, smem_w4);
     } else if constexpr (STAGED) {
       store_tile_staged<EPI, TJ>(acc, bias, ep, M, N, tm, tn, wm, wn, lane, tid, smem_w4);
     } else {
@@ -1005,10 +1050,12 @@ void gemm_w4_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
   }
 }
 
-// The split-K tail of a hybrid four-wave launch: adds the splits' partial
-// sums of each tail tile, then the bias and the epilogue, four consecutive
-// columns per thread (they lie in one head of one block for the QKV
-// projection, as the head dim is a multiple of four).
+// The split-K tail of a hybrid four-wave launch: adds the partial sums of
+// each tail tile in K order, then the bias and the epilogue, four
+// consecutive columns per thread (they lie in one head of one block for the
+// QKV projection, as the head dim is a multiple of four).  An even split
+// leaves `splits` partial tiles per tail tile, split-major (tile t's at t,
+// t + n_tail, ...); a main-and-helper tail two (t, n_tail + t).
 template <int EPI, int BN>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restrict__ part,
                                                           int splits, TileMap map,
@@ -1018,6 +1065,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restric
   const int t = blockIdx.x;
   int tm, tn;
   tile_of(map.tile_base + t, map.tiles_m, map.ntiles, map.group, tm, tn);
+  const int count = map.sk_kt > 0 ? 2 : splits;
   const size_t plane = (size_t)map.n_tail * BM * BN;
   for (int idx = blockIdx.y * 256 + threadIdx.x; idx < BM * Q; idx += gridDim.y * 256) {
     const int r = idx / Q, c = (idx - r * Q) * 4;
@@ -1025,7 +1073,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restric
     if (m >= M || n >= N) continue;
     const float* p = part + (size_t)t * BM * BN + (size_t)r * BN + c;
     float4 v = *reinterpret_cast<const float4*>(p);
-    for (int sp = 1; sp < splits; ++sp) {
+    for (int sp = 1; sp < count; ++sp) {
       const float4 u = *reinterpret_cast<const float4*>(p + sp * plane);
       v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
     }
@@ -1485,21 +1533,53 @@ static int raster_group(int tiles_m) {
   return env_int("ORCA_GEMM_GROUP", tiles_m >= 12 ? 8 : 0);
 }
 
-// Hybrid four-wave launch: when the last round of resident workgroups is at
-// most half full, the tiles of every full round run as usual and the last
-// round's n_tail tiles run with K split by 2-4 (each split an even number
-// of at least 16 K steps), so that round ends in a fraction of a tile's
-// time; their fp32 partial sums (n_tail * splits tiles) are added by
-// tail_reduce_kernel, which applies the epilogue.  On the 175B layer shape
-// at 3,698 rows: QKV 2,160 tiles = 8 rounds + 112 tiles (2 splits), FFN1
-// 2,880 = 11 rounds + 64 (4 splits).  ORCA_GEMM_TAIL=0 turns it off.
+// Hybrid four-wave launch: the tiles of every full round run as usual, and
+// the last round's n_tail tiles run split over K so that the round keeps
+// every CU busy; their fp32 partial sums are added by tail_reduce_kernel,
+// which applies the epilogue.  ORCA_GEMM_TAIL=0 turns it off.
+// * When that round is at most half full: K split by 2-4 (each split an
+//   even number of at least 16 K steps), so the round ends in a fraction of
+//   a tile's time.  On the 175B layer shape at 3,698 rows: QKV 2,160 tiles
+//   = 8 rounds + 112 tiles (2 splits), FFN1 2,880 = 11 rounds + 64 (4).
+// * Fuller: the main-and-helper split (sk_segment) on one workgroup per CU,
+//   NUM_CU - n_tail of them helpers taking c = ceil(n_tail / helpers) tile
+//   remainders each; x balances a main's x steps against a helper's
+//   c (kt - x), plus 4 steps for each further segment's loads and partial
+//   store.  Taken where the round shrinks by ORCA_GEMM_SK_MIN (64) K steps
+//   or more.  On the 175B layer: FFN2 (720 tiles = 2 rounds + 208, 768 steps
+//   a tile: 48 helpers, c = 5, x = 644), not the output projection (192
+//   steps, x = 160: 32 steps saved).
 struct TailPlan {
   int n_dp, n_tail, splits, per;
+  int sk_kt;     // main-and-helper: K steps per tile (0: an even split)
+  int wgs;       // tail workgroups
+  size_t slots;  // fp32 partial tiles in the workspace
 };
 static bool tail_plan(int tiles, int kt, TailPlan& t) {
   if (!env_int("ORCA_GEMM_TAIL", 1)) return false;
   const int rem = tiles % NUM_CU;
-  if (tiles < NUM_CU || rem == 0 || rem > NUM_CU / 2 || kt % 2) return false;
+  if (tiles < NUM_CU || rem == 0 || kt % 2) return false;
+  t.n_tail = rem;
+  t.n_dp = tiles - rem;
+  t.sk_kt = 0;
+  if (rem > NUM_CU / 2) {
+    const int helpers = NUM_CU - rem, c = (rem + helpers - 1) / helpers;
+    int best_x = 0, best = kt;
+    for (int x = 2; x <= kt - 2; x += 2) {   // even: a segment runs its K steps in pairs
+      const int span = std::max(x, c * (kt - x) + 4 * (c - 1));
+      if (span <= best) {
+        best = span;
+        best_x = x;
+      }
+    }
+    if (best_x == 0 || kt - best < env_int("ORCA_GEMM_SK_MIN", 64)) return false;
+    t.per = best_x;
+    t.sk_kt = kt;
+    t.wgs = NUM_CU;
+    t.splits = 2;
+    t.slots = 2 * (size_t)rem;
+    return true;
+  }
   int sp = std::min(4, NUM_CU / rem);
   while (sp > 1 && kt / sp < 16) --sp;
   if (sp < 2) return false;
@@ -1507,8 +1587,8 @@ static bool tail_plan(int tiles, int kt, TailPlan& t) {
   per += per & 1;
   t.splits = (kt + per - 1) / per;
   t.per = per;
-  t.n_tail = rem;
-  t.n_dp = tiles - rem;
+  t.wgs = rem;
+  t.slots = (size_t)rem * t.splits;
   return t.splits >= 2;
 }
 // the four-wave forms' tile count (bn: 256 or 192)
@@ -1565,8 +1645,7 @@ size_t linear_workspace_bytes(int dtype, int m, int n, int k) {
   if ((v == 12 || v == 13) && w4_ok(m, n, k)) {
     const int bn = v == 12 ? 256 : 192;
     TailPlan t;
-    if (tail_plan(w4_tiles(m, n, bn), k / BK, t))
-      return (size_t)t.n_tail * t.splits * 256 * bn * sizeof(float);
+    if (tail_plan(w4_tiles(m, n, bn), k / BK, t)) return t.slots * 256 * bn * sizeof(float);
   }
   return 0;
 }
@@ -1653,8 +1732,8 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
           const int tiles_m = (m + 255) / 256, tiles = w4_tiles(m, n, bn);
           TileMap map{tiles_m, tiles, raster_group(tiles_m), 0, k / BK, 0};
           TailPlan t;
-          const bool tail = tail_plan(tiles, k / BK, t) &&
-                            ws && ws_bytes >= (size_t)t.n_tail * t.splits * 256 * bn * 4;
+          const bool tail = tail_plan(tiles, k / BK, t) && ws &&
+                            ws_bytes >= t.slots * 256 * bn * sizeof(float);
           if (tail) map.ntiles = tiles;
           auto kern = v == 12 ? gemm_w4_kernel<EPI, 4> : gemm_w4_kernel<EPI, 3>;
           const int n_dp = tail ? t.n_dp : tiles;
@@ -1663,11 +1742,12 @@ static void launch_typed(int dtype, const void* a, const void* w, const void* bi
           hipLaunchKernelGGL(kern, dim3(map.persist ? NUM_CU : n_dp), dim3(W4_THREADS), 0, s,
                              (const bf16*)a, (const bf16*)w, (const bf16*)bias, ep, m, n, k, map);
           if (tail) {
-            TileMap tm{tiles_m, tiles, map.group, t.n_dp, t.per, t.n_tail};
+            TileMap tm{tiles_m, tiles, map.group, t.n_dp, t.per, t.n_tail, 0, t.sk_kt};
             EpiParams pp{};
             pp.out = ws;
             auto pk = v == 12 ? gemm_w4_kernel<EPI_PARTIAL, 4> : gemm_w4_kernel<EPI_PARTIAL, 3>;
-            hipLaunchKernelGGL(pk, dim3(t.n_tail, t.splits), dim3(W4_THREADS), 0, s,
+            hipLaunchKernelGGL(pk, t.sk_kt ? dim3(t.wgs) : dim3(t.n_tail, t.splits),
+                               dim3(W4_THREADS), 0, s,
                                (const bf16*)a, (const bf16*)w, (const bf16*)bias, pp, m, n, k,
                                tm);
             auto rk = v == 12 ? tail_reduce_kernel<EPI, 256> : tail_reduce_kernel<EPI, 192>;

@@ -426,23 +426,40 @@ def test_planner_split_counts(m, n, k, splits):
 
 
 # the split tail of the four-wave launches, seen through its workspace
-# (fp32 partial tiles, tail tiles x splits x 256 x 256 or 256 x 192): only
-# when the last round of 256 workgroups is at most half full
-@pytest.mark.parametrize("m,n,k,tail_tiles,splits,bn", [
-    (3698, 36864, 12288, 112, 2, 256),    # 175B layer QKV: 2,160 tiles = 8 rounds + 112
-    (3698, 49152, 12288, 64, 4, 256),     # FFN1: 2,880 = 11 rounds + 64
-    (3698, 12288, 12288, 0, 0, 256),      # output projection: 720 = 2 rounds + 208
-    (3698, 12288, 49152, 0, 0, 256),      # FFN2: the same tiles
-    (2176, 15360, 5120, 0, 0, 192),       # 13B: 720 tiles, 2 rounds + 208
-    (1100, 15360, 4096, 44, 4, 256),      # the GPU test's shapes
+# (fp32 partial tiles of 256 x 256 or 256 x 192): when the last round of 256
+# workgroups is at most half full, tail tiles x splits of them; fuller, a
+# main-and-helper tail leaves two per tail tile, where it saves 64 K steps
+# or more
+@pytest.mark.parametrize("m,n,k,slots,bn", [
+    (3698, 36864, 12288, 112 * 2, 256),   # 175B layer QKV: 2,160 tiles = 8 rounds + 112
+    (3698, 49152, 12288, 64 * 4, 256),    # FFN1: 2,880 = 11 rounds + 64
+    (3698, 12288, 12288, 0, 256),         # output projection: 720 = 2 rounds + 208, 192 steps
+    (3698, 12288, 49152, 2 * 208, 256),   # FFN2: the same tiles, 768 steps: 644 a main
+    (2176, 15360, 5120, 0, 192),          # 13B: 720 tiles, 2 rounds + 208, 80 steps
+    (1100, 15360, 4096, 44 * 4, 256),     # the GPU tests' shapes
 ])
-def test_planner_split_tail(m, n, k, tail_tiles, splits, bn, monkeypatch):
+def test_planner_split_tail(m, n, k, slots, bn, monkeypatch):
     monkeypatch.delenv("ORCA_GEMM_TAIL", raising=False)
+    monkeypatch.delenv("ORCA_GEMM_SK_MIN", raising=False)
     if (m, n, k) == (1100, 15360, 4096):
         monkeypatch.setenv("ORCA_GEMM_VARIANT", "12")
     else:
         monkeypatch.delenv("ORCA_GEMM_VARIANT", raising=False)
-    assert L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k) == \
-        tail_tiles * splits * 256 * bn * 4
+    assert L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k) == slots * 256 * bn * 4
     monkeypatch.setenv("ORCA_GEMM_TAIL", "0")
+    assert L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k) == 0
+
+
+# main-and-helper tails below the default threshold (ORCA_GEMM_SK_MIN=0)
+@pytest.mark.parametrize("m,n,k,variant,slots,bn", [
+    (1100, 20480, 2048, "12", 2 * 144, 256),   # 400 tiles = 256 + 144, 32 steps a tile
+    (1100, 15168, 2560, "13", 2 * 139, 192),   # 395 = 256 + 139, 40 steps
+    (1100, 20032, 2048, "12", 2 * 139, 256),   # 395 (last column tile 64 wide)
+])
+def test_planner_main_helper_tail(m, n, k, variant, slots, bn, monkeypatch):
+    monkeypatch.delenv("ORCA_GEMM_TAIL", raising=False)
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", variant)
+    monkeypatch.setenv("ORCA_GEMM_SK_MIN", "0")
+    assert L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k) == slots * 256 * bn * 4
+    monkeypatch.delenv("ORCA_GEMM_SK_MIN")
     assert L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k) == 0

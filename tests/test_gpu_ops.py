@@ -385,6 +385,88 @@ def test_hybrid_split_tail(variant, n, epi, monkeypatch):
     assert rel_err(outs[0][rows], ref) < TOL["bf16"]
 
 
+# main-and-helper tails (the last round more than half full;
+# ORCA_GEMM_SK_MIN=0 takes them at these small K): (1100, 20480, 2048) on
+# 256 x 256: 400 tiles = 256 + 144, 32 K steps a tile, 144 mains taking 24,
+# 112 helpers the other 8 of one or two tiles each; (1100, 15168, 2560) on
+# 256 x 192: 395 = 256 + 139, 40 steps, mains 28; (1100, 20032, 2048): 395
+# tiles, the last column tile 64 wide.  The workspace starts as NaN (a
+# partial tile the reduce reads but no workgroup wrote shows), the output is
+# compared with the launch without a tail and with the oracle on sampled
+# rows, and a second call gives the same bits (the partial tiles are added
+# in a fixed order).
+@pytest.mark.parametrize("m,n,k,variant", [
+    (1100, 20480, 2048, "12"), (1100, 15168, 2560, "13"), (1100, 20032, 2048, "12")])
+@pytest.mark.parametrize("epi", [L.ORCA_EPI_BIAS, L.ORCA_EPI_BIAS_GELU, L.ORCA_EPI_BIAS_RESID])
+def test_main_helper_tail(m, n, k, variant, epi, monkeypatch):
+    print(f"case main-and-helper tail variant {variant} m={m} n={n} k={k} epi={epi}", flush=True)
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", variant)
+    monkeypatch.setenv("ORCA_GEMM_SK_MIN", "0")
+    rng = np.random.default_rng(n + k + epi)
+    a = draw(rng, (m, k), 1.0, "bf16")
+    w = draw(rng, (n, k), 0.02 * 32 / np.sqrt(k), "bf16")
+    b = draw(rng, n, 0.02, "bf16")
+    init = rng.standard_normal((m, n)).astype(np.float32) if epi == L.ORCA_EPI_BIAS_RESID else None
+    nb = L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k)
+    assert nb > 0, "expected a main-and-helper tail"
+    ad, wd, bd = dev(a, "bf16"), dev(w, "bf16"), dev(b, "bf16")
+    outs = []
+    for tail in ("1", "1", "0"):
+        monkeypatch.setenv("ORCA_GEMM_TAIL", tail)
+        out = (torch.from_numpy(init).to(DEV) if init is not None
+               else torch.empty((m, n), dtype=torch.bfloat16, device=DEV))
+        ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device=DEV)
+        L.orca_op_linear(L.ORCA_BF16, epi, ad, wd, bd, out, m, n, k, ws, nb)
+        outs.append(host(out))
+    assert np.isfinite(outs[0]).all()
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert rel_err(outs[0], outs[2]) < 1e-2
+    rows = np.concatenate([np.arange(0, 8), np.arange(700, 708), np.arange(m - 40, m)])
+    ref = om.linear(a[rows].astype(np.float64), w.astype(np.float64), b.astype(np.float64))
+    if epi == L.ORCA_EPI_BIAS_GELU:
+        ref = om.gelu_tanh(ref)
+    if init is not None:
+        ref = init[rows].astype(np.float64) + ref
+    assert rel_err(outs[0][rows], ref) < TOL["bf16"]
+
+
+def test_main_helper_tail_qkv(monkeypatch):
+    """The QKV projection with a main-and-helper tail (hidden 7168: 5 x 84 =
+    420 tiles = 256 + 164, 112 K steps a tile): the same Q rows and pool
+    slots as the launch without a tail, and the oracle's on sampled rows."""
+    m, hidden, heads = 1100, 7168, 56
+    d, cap = hidden // heads, 1500
+    monkeypatch.setenv("ORCA_GEMM_VARIANT", "12")
+    monkeypatch.setenv("ORCA_GEMM_SK_MIN", "0")
+    nb = L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, 3 * hidden, hidden)
+    assert nb > 0
+    rng = np.random.default_rng(7)
+    a = draw(rng, (m, hidden), 1.0, "bf16")
+    w = draw(rng, (3 * hidden, hidden), 0.02, "bf16")
+    b = draw(rng, 3 * hidden, 0.02, "bf16")
+    dst = rng.permutation(cap)[:m].astype(np.int32)
+    res = []
+    for tail in ("1", "0"):
+        monkeypatch.setenv("ORCA_GEMM_TAIL", tail)
+        kvp = torch.zeros((heads, cap, 2, d), dtype=torch.bfloat16, device=DEV)
+        kp, vp = kvp[:, :, 0], kvp[:, :, 1]
+        q = torch.empty((m, hidden), dtype=torch.bfloat16, device=DEV)
+        ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device=DEV)
+        L.orca_op_qkv(L.ORCA_BF16, dev(a, "bf16"), dev(w, "bf16"), dev(b, "bf16"), q, kvp,
+                      torch.from_numpy(dst).to(DEV), m, hidden, heads, cap, ws, nb)
+        res.append((host(q), host(kp), host(vp)))
+    for x, y in zip(res[0], res[1]):
+        assert np.isfinite(x).all()
+        assert rel_err(x, y) < 1e-2
+    rows = np.concatenate([np.arange(0, 4), np.arange(m - 20, m)])
+    ref = om.linear(a[rows].astype(np.float64), w.astype(np.float64), b.astype(np.float64))
+    assert rel_err(res[0][0][rows], ref[:, :hidden]) < TOL["bf16"]
+    kref = ref[:, hidden:2 * hidden].reshape(len(rows), heads, d).transpose(1, 0, 2)
+    vref = ref[:, 2 * hidden:].reshape(len(rows), heads, d).transpose(1, 0, 2)
+    assert rel_err(res[0][1][:, dst[rows]], kref) < TOL["bf16"]
+    assert rel_err(res[0][2][:, dst[rows]], vref) < TOL["bf16"]
+
+
 def test_hybrid_split_tail_qkv(monkeypatch):
     """The QKV projection's split tail: the same Q rows and pool slots as the
     launch without it, and the oracle's on sampled rows."""
