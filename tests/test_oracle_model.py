@@ -15,6 +15,7 @@ import torch.nn.functional as F
 
 from oracle import model as om
 from orca_selective_iteration_amd import synth
+from tests.util import golden
 
 pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
 
@@ -185,8 +186,11 @@ def test_selective_equals_alone_equals_padded(layers):
 
 
 def test_tiny_figure_batch_equalities():
+    g = golden("houmin_figure_batch")
     w = synth.workload("tiny-fp32")
-    assert w.rows == 7 and w.q_len == [1, 1, 2, 3] and w.kv_len == [3, 4, 0, 0]
+    assert w.rows == g["batch_rows"] and w.q_len == [1, 1, g["x3_prompt_tokens"],
+                                                      g["x4_prompt_tokens"]]
+    assert w.kv_len[0] == g["x1_cached_tokens"] and w.kv_len[2:] == [0, 0]
     hin = synth.host_inputs(w, seed=0)
     p, c, x = f64_params(hin), f64_caches(hin), hin.x.astype(np.float64)
     reqs = reqs_of(w)
@@ -283,13 +287,19 @@ def test_chunked_prompt_equals_whole_prompt(cuts):
 
 def test_shape_pins_of_the_figure():
     """[7,H] in, [7,3H] after the fused QKV Linear, [7,H] after the merge
-    (houmin 3.1.2); [5,H] for x3+x4 alone; 128+64+256 = 448 rows
-    (estelledc case 2)."""
+    (houmin 3.1.2); [5,H] for x3 + x4 alone; 128 + 64 + 256 = 448 rows
+    (estelledc case 2).  Values from tests/golden/houmin_figure_batch.txt and
+    notes_case2_flattened_rows.txt."""
+    g = golden("houmin_figure_batch")
     w = synth.workload("tiny-fp32")
     hin = synth.host_inputs(w)
     p = hin.params[0]
     a = om.layer_norm(hin.x, p["ln1_g"], p["ln1_b"], 1e-5)
-    assert om.linear(a, p["w_qkv"], p["b_qkv"]).shape == (7, 3 * 64)
-    assert sum(w.q_len[2:]) == 5
-    w448 = synth.custom_workload(1, 8, 2, 16, "f32", [128, 64, 256], [0, 0, 0])
-    assert w448.rows == 448 and w448.q_offset == [0, 128, 192]
+    assert a.shape == (g["batch_rows"], 64)
+    assert om.linear(a, p["w_qkv"], p["b_qkv"]).shape == (g["batch_rows"],
+                                                           g["qkv_width_multiple"] * 64)
+    assert sum(w.q_len[2:]) == g["x3_prompt_tokens"] + g["x4_prompt_tokens"]
+    c2 = golden("notes_case2_flattened_rows")
+    lens = c2["prefill_lengths"]
+    w448 = synth.custom_workload(1, 8, 2, 16, "f32", lens, [0] * len(lens))
+    assert w448.rows == c2["flattened_rows"] and w448.q_offset == [0, lens[0], lens[0] + lens[1]]

@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 from oracle import sched as osch
+from tests.util import golden
 
 
 def run(out_lens, slots, policy, arrivals=None, prompt=1, budget=10**9, kv=10**12,
@@ -21,32 +22,38 @@ def run(out_lens, slots, policy, arrivals=None, prompt=1, budget=10**9, kv=10**1
 # ------------------------------------------------- the pages' worked examples
 
 def test_ultralytics_eight_requests_four_slots():
-    """ultralytics.com glossary "Continuous Batching": output lengths
-    [5,50,8,12,40,3,30,7] on 4 slots: static 90 steps with 43% of slots busy,
-    continuous 50 steps with 78% busy."""
-    lens = [5, 50, 8, 12, 40, 3, 30, 7]
-    _, st = run(lens, 4, "static")
-    _, co = run(lens, 4, "iteration")
-    assert st.iterations == 90 and co.iterations == 50
-    assert st.busy_rows == co.busy_rows == 155
-    assert round(100 * st.busy_rows / (st.iterations * 4)) == 43
-    assert round(100 * co.busy_rows / (co.iterations * 4)) == 78
+    """ultralytics.com glossary "Continuous Batching": the eight requests of
+    its simulation on four slots, with the step counts and slot use the page
+    states (tests/golden/glossary_eight_requests.txt)."""
+    g = golden("glossary_eight_requests")
+    lens, slots = g["output_lengths"], g["slots"]
+    _, st = run(lens, slots, "static")
+    _, co = run(lens, slots, "iteration")
+    assert st.iterations == g["static_steps"] and co.iterations == g["continuous_steps"]
+    assert st.busy_rows == co.busy_rows == sum(lens)
+    assert round(100 * st.busy_rows / (st.iterations * slots)) == g["static_busy_percent"]
+    assert round(100 * co.busy_rows / (co.iterations * slots)) == g["continuous_busy_percent"]
 
 
 def test_estelledc_three_slot_timeline():
-    """estelledc.github.io case 1: A=100, B=10, C=50 tokens on 3 slots.
-    Continuous: D starts at step 11, E at 51, F at 101 (1-based steps).
-    Static: B's slot idles over steps 11-50, C's over 51-100."""
-    lens = [100, 10, 50, 200, 200, 200]        # A B C D E F
-    s, _ = run(lens, 3, "iteration")
-    starts = {i: s.requests[i].admitted_at + 1 for i in range(6)}
-    assert starts[3] == 11 and starts[4] == 51 and starts[5] == 101
-    s2, res = run(lens, 3, "static")
-    for step in range(11, 51):
+    """estelledc.github.io notes, case 1: A, B, C on three slots with D, E, F
+    queued (tests/golden/notes_case1_three_slots.txt; D-F's lengths are not
+    given: 200 each, longer than A).  Continuous: D, E, F start at the steps
+    the page gives (1-based).  Static: B's slot, then C's, idles over the
+    spans it gives, and D waits for the whole first batch."""
+    g = golden("notes_case1_three_slots")
+    lens = g["lengths_abc"] + [200, 200, 200]        # A B C D E F
+    s, _ = run(lens, g["slots"], "iteration")
+    starts = [s.requests[i].admitted_at + 1 for i in (3, 4, 5)]
+    assert starts == g["continuous_start_def"]
+    s2, res = run(lens, g["slots"], "static")
+    b0, b1 = g["static_b_idle"]
+    c0, c1 = g["static_c_idle"]
+    for step in range(b0, b1 + 1):
         assert res.log[step - 1][1] == (0, 2)
-    for step in range(51, 101):
+    for step in range(c0, c1 + 1):
         assert res.log[step - 1][1] == (0,)
-    assert s2.requests[3].admitted_at + 1 == 101
+    assert s2.requests[3].admitted_at + 1 == c1 + 1
 
 
 def test_static_batch_lasts_longest_member():

@@ -1,4 +1,7 @@
-"""Shared helpers of the test-suite (comparison metric, oracle adapters)."""
+"""Shared helpers of the test-suite (comparison metric, oracle adapters,
+the pages' printed values under tests/golden/)."""
+from pathlib import Path
+
 import numpy as np
 
 from oracle import model as om
@@ -33,3 +36,21 @@ def f64_params(params):
 def f64_caches(caches):
     return [[(np.asarray(k, np.float64), np.asarray(v, np.float64)) for k, v in per]
             for per in caches]
+
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+def golden(name):
+    """Values a page prints for a worked example, from tests/golden/<name>.txt:
+    `key: v1 v2 ...` lines of integers ('#' starts a comment).  A key with one
+    value maps to an int, with several to a list."""
+    out = {}
+    for line in (GOLDEN / f"{name}.txt").read_text(encoding="utf-8").splitlines():
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        key, vals = line.split(":", 1)
+        nums = [int(v) for v in vals.split()]
+        out[key.strip()] = nums[0] if len(nums) == 1 else nums
+    return out
