@@ -253,8 +253,11 @@ typedef enum {
  *   - problems whose output tiles are too few to fill the GPU (chiefly
  *     batches of few rows, made mostly of increment rows: the weights are
  *     streamed once and the arithmetic is light) split every tile;
- *   - large problems whose last round of tiles would leave more than half
- *     the GPU idle split only that round's tiles (the rest run unsplit).
+ *   - large problems whose last round of tiles would leave CUs idle split
+ *     only that round's tiles (the rest run unsplit): evenly when the round
+ *     is at most half full; fuller, a leading part of each tile's K on one
+ *     workgroup and the rest on the CUs the round leaves idle, where the
+ *     round shrinks by enough K steps to pay for the partial sums.
  * Otherwise every tile runs over the whole of K and the workspace is not
  * touched.  Every path accumulates in fp32; only the summation order
  * differs.  orca_op_linear_workspace_bytes returns 0 where no split applies
