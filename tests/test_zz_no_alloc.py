@@ -80,3 +80,40 @@ def test_noalloc_rejects_problems_past_its_buffer():
     assert "static" in str(e.value)
     torch.cuda.synchronize()
     assert bool((out == 5.0).all())
+
+
+def test_noalloc_runs_a_tail_past_its_buffer_without_it():
+    """A tiled launch whose last round takes a main-and-helper split by
+    default (1100 x 20480 x 16384 on 256 x 256 tiles: 400 tiles = 256 + 144,
+    256 K steps a tile) needs 72 MiB of partial tiles, past the static
+    buffer: the no-allocation entry point runs every tile over the whole of
+    K instead, the same bits as orca_op_linear without a workspace; the
+    split launch agrees to rounding, and sampled rows meet the oracle."""
+    m, n, k = 1100, 20480, 16384
+    epi = L.ORCA_EPI_BIAS_RESID
+    nb = L.orca_op_linear_workspace_bytes(L.ORCA_BF16, m, n, k)
+    assert nb == 2 * 144 * 256 * 256 * 4 > L.ORCA_NOALLOC_SCRATCH_BYTES
+    print(f"case noalloc tail past the buffer m={m} n={n} k={k}", flush=True)
+    rng = np.random.default_rng(11)
+    def bf(shape, scale):
+        return synth.round_to_bf16((scale * rng.standard_normal(shape)).astype(np.float32))
+    a_h, w_h, b_h = bf((m, k), 1.0), bf((n, k), 0.02 * 32 / np.sqrt(k)), bf(n, 0.02)
+    init = rng.standard_normal((m, n)).astype(np.float32)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV, torch.bfloat16)
+    a, w, b = t(a_h), t(w_h), t(b_h)
+    out_plain = _out(m, n, epi, init)
+    L.orca_op_linear(L.ORCA_BF16, epi, a, w, b, out_plain, m, n, k)
+    out_na = _out(m, n, epi, init)
+    L.orca_op_linear_noalloc(L.ORCA_BF16, epi, a, w, b, out_na, m, n, k)
+    ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    out_tail = _out(m, n, epi, init)
+    L.orca_op_linear(L.ORCA_BF16, epi, a, w, b, out_tail, m, n, k, ws, nb)
+    assert np.array_equal(_bits(out_plain), _bits(out_na))
+    na, tail = out_na.cpu().numpy(), out_tail.cpu().numpy()
+    assert np.isfinite(tail).all()
+    assert rel_err(tail, na) < 1e-4
+    rows = np.array([0, 1, 255, 256, 700, m - 2, m - 1])
+    ref = init[rows].astype(np.float64) + om.linear(
+        a_h[rows].astype(np.float64), w_h.astype(np.float64), b_h.astype(np.float64))
+    assert rel_err(na[rows], ref) < TOL["bf16"]
+    del ws
